@@ -1,0 +1,10 @@
+"""fp64 CPU oracle for the exact attention forward pass.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py``, never by the product path.
+"""
+from .attention import (as_f64, attention_forward, boundary_scale,
+                        streaming_attention)
+
+__all__ = ["as_f64", "attention_forward", "boundary_scale",
+           "streaming_attention"]
