@@ -1,0 +1,116 @@
+/*
+ * fa_mi355x.h -- C ABI of the MI355X (gfx950) FlashAttention forward library.
+ *
+ * The library computes exact attention, O = softmax(scale * Q K^T) V, together
+ * with the natural-log log-sum-exp of every score row, in one fused HIP kernel
+ * that walks K and V tile by tile with an online softmax (running row maximum
+ * and running sum, accumulator rescaled when the maximum grows), so the N x N
+ * score matrix is never written to HBM.  Sources: "FlashAttention" (Chapter 15,
+ * vizuara), sections "Standard vs Flash Attention" (the four steps: load tiles,
+ * tile scores, online softmax, accumulate O and write it once) and "The Tiling
+ * Strategy"; "FlashAttention, Playable", EP 03 (tiling) and EP 04 (online
+ * softmax); "FlashAttention: Tiled & Fused", hero diagram (O written once,
+ * running statistics kept on chip).
+ *
+ * Conventions shared by every entry point
+ *   - All functions are extern "C", never throw, and report errors through
+ *     fa_status.  No entry point allocates device memory or keeps a pointer
+ *     after it returns.
+ *   - Argument checks run before any HIP runtime call, so a host without a
+ *     GPU can exercise every error path.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_MI355X_ABI_VERSION 1
+
+typedef enum {
+  FA_F32 = 0,   /* IEEE binary32 */
+  FA_F16 = 1,   /* IEEE binary16 */
+  FA_BF16 = 2   /* bfloat16 */
+} fa_dtype;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,       /* a required pointer is NULL */
+  FA_ERR_SHAPE = 2,      /* B, H or N negative, or an index would overflow */
+  FA_ERR_HEAD_DIM = 3,   /* d is not a supported head dimension (64, 128) */
+  FA_ERR_DTYPE = 4,      /* dtype is not an fa_dtype value */
+  FA_ERR_ALIGN = 5,      /* a pointer is not 16-byte aligned */
+  FA_ERR_SCALE = 6,      /* scale is NaN or infinite */
+  FA_ERR_ALIAS = 7,      /* o or lse overlaps an input or each other */
+  FA_ERR_NO_DEVICE = 8,  /* no HIP device is usable */
+  FA_ERR_ARCH = 9,       /* the current device is not gfx950 */
+  FA_ERR_HIP = 10        /* the HIP runtime reported an error (see last_error) */
+} fa_status;
+
+/*
+ * flash_attn_fwd -- exact attention forward pass for every (batch, head).
+ *
+ * For each b < B, h < H and query row i < N:
+ *   s_ij   = scale * sum_c q[b,h,i,c] * k[b,h,j,c]      for visible keys j
+ *   o[b,h,i,:] = sum_j softmax_j(s_ij) * v[b,h,j,:]
+ *   lse[b,h,i] = ln(sum_j exp(s_ij))
+ * Visible keys are j < N, and with causal != 0 only j <= i (lower-triangular
+ * mask, diagonal included; the pages do not treat masking, so this is the
+ * plain reading of a causal mask).
+ *
+ * Arguments
+ *   q, k, v  device pointers, read only, contiguous row-major [B, H, N, d]
+ *            arrays of `dtype` (element [b,h,n,c] at ((b*H + h)*N + n)*d + c).
+ *   o        device pointer, contiguous [B, H, N, d] of `dtype`; fully
+ *            overwritten (rounded to nearest even from fp32).
+ *   lse      device pointer, contiguous [B, H, N] float32; fully overwritten.
+ *   B, H, N  batch, heads and sequence length, each >= 0.  If any is 0 the
+ *            call returns FA_OK without touching the device.
+ *   d        head dimension: 64 or 128.
+ *   scale    finite float multiplying Q K^T (usually 1/sqrt(d)); negative and
+ *            zero values are allowed.
+ *   causal   0 = every key visible, nonzero = lower-triangular mask.
+ *   dtype    element type of q, k, v and o.  FA_F16 and FA_BF16 run both
+ *            products on MFMA with fp32 accumulation and round the softmax
+ *            weights to `dtype` before the second product; FA_F32 keeps every
+ *            step in fp32.
+ *   stream   hipStream_t to enqueue on, passed as void*; NULL is the null
+ *            stream of the current device.
+ *
+ * Ownership and synchronisation: the caller owns all five buffers, which must
+ * live on the current HIP device and be 16-byte aligned.  o and lse must not
+ * overlap each other or q, k, v.  The call enqueues one kernel and returns
+ * without synchronising; results are valid once `stream` has completed.  It is
+ * reentrant and keeps no state between calls apart from a per-device cache of
+ * the architecture check and a thread-local error string.
+ *
+ * Errors: argument errors are returned before any HIP call (FA_ERR_NULL,
+ * FA_ERR_SHAPE, FA_ERR_HEAD_DIM, FA_ERR_DTYPE, FA_ERR_ALIGN, FA_ERR_SCALE,
+ * FA_ERR_ALIAS).  Then FA_ERR_NO_DEVICE or FA_ERR_ARCH if the current device
+ * cannot run the gfx950 kernel, and FA_ERR_HIP if the launch fails; the HIP
+ * error text is then available from flash_attn_last_error().  Nothing is
+ * enqueued when an error is returned.
+ */
+fa_status flash_attn_fwd(const void* q, const void* k, const void* v,
+                         void* o, float* lse,
+                         int64_t B, int64_t H, int64_t N, int64_t d,
+                         float scale, int causal,
+                         fa_dtype dtype, void* stream);
+
+/* Static, never-NULL description of a status code. */
+const char* flash_attn_status_str(fa_status status);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* flash_attn_last_error(void);
+
+/* FA_MI355X_ABI_VERSION of the loaded library. */
+int flash_attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

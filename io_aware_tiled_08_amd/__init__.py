@@ -1,1 +1,11 @@
-"""MI355X-native FlashAttention forward pass (gfx950 HIP kernels behind a C ABI)."""
+"""MI355X-native FlashAttention forward pass.
+
+The computation runs in hand-written gfx950 HIP kernels inside
+``libfa_mi355x.so`` (C ABI: include/fa_mi355x.h); this package only marshals
+torch tensors into that ABI.
+"""
+from .binding import (FA_BF16, FA_F16, FA_F32, FlashAttnError, flash_attn_fwd,
+                      flash_attn_fwd_ptr, last_error, lib)
+
+__all__ = ["FA_BF16", "FA_F16", "FA_F32", "FlashAttnError", "flash_attn_fwd",
+           "flash_attn_fwd_ptr", "last_error", "lib"]

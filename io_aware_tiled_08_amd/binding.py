@@ -1,0 +1,136 @@
+"""ctypes binding of libfa_mi355x.so.
+
+Argument marshalling only: every step of the forward pass runs in the HIP
+kernels behind the C ABI declared in include/fa_mi355x.h.  torch supplies the
+device memory and the stream; nothing here computes attention, and there is no
+fallback: if the library is missing or the device is not gfx950 the call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+from typing import Optional, Tuple
+
+from .build import LIB_PATH
+
+FA_F32, FA_F16, FA_BF16 = 0, 1, 2
+STATUS = {
+    0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEAD_DIM",
+    4: "FA_ERR_DTYPE", 5: "FA_ERR_ALIGN", 6: "FA_ERR_SCALE", 7: "FA_ERR_ALIAS",
+    8: "FA_ERR_NO_DEVICE", 9: "FA_ERR_ARCH", 10: "FA_ERR_HIP",
+}
+STATUS_CODE = {name: code for code, name in STATUS.items()}
+EXPORTS = ("flash_attn_fwd", "flash_attn_status_str", "flash_attn_last_error",
+           "flash_attn_abi_version")
+ABI_VERSION = 1
+
+_lib = None
+_lock = threading.Lock()
+
+
+class FlashAttnError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        self.name = STATUS.get(status, f"status {status}")
+        super().__init__(f"{self.name}: {detail}" if detail else self.name)
+
+
+def library_path() -> str:
+    return os.environ.get("FA_MI355X_LIB", LIB_PATH)
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfa_mi355x.so once and declare its signatures."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            path = library_path()
+            if not os.path.exists(path):
+                raise RuntimeError(
+                    f"{path} is not built; build it with "
+                    "`python -m io_aware_tiled_08_amd.build` (needs hipcc)")
+            L = ctypes.CDLL(path)
+            L.flash_attn_fwd.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 4 + [
+                ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+            L.flash_attn_fwd.restype = ctypes.c_int
+            L.flash_attn_status_str.argtypes = [ctypes.c_int]
+            L.flash_attn_status_str.restype = ctypes.c_char_p
+            L.flash_attn_last_error.argtypes = []
+            L.flash_attn_last_error.restype = ctypes.c_char_p
+            L.flash_attn_abi_version.argtypes = []
+            L.flash_attn_abi_version.restype = ctypes.c_int
+            if L.flash_attn_abi_version() != ABI_VERSION:
+                raise RuntimeError(f"{path}: ABI version {L.flash_attn_abi_version()}, "
+                                   f"binding expects {ABI_VERSION}")
+            _lib = L
+        return _lib
+
+
+def last_error() -> str:
+    return lib().flash_attn_last_error().decode()
+
+
+def flash_attn_fwd_ptr(q: int, k: int, v: int, o: int, lse: int, B: int, H: int,
+                       N: int, d: int, scale: float, causal: bool, dtype: int,
+                       stream: int = 0) -> int:
+    """Raw call of the C entry point on integer addresses; returns the status."""
+    return lib().flash_attn_fwd(q, k, v, o, lse, B, H, N, d, scale, int(bool(causal)),
+                                dtype, stream)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}; expected float32, float16 or bfloat16")
+    return codes[t.dtype]
+
+
+def flash_attn_fwd(q, k, v, o=None, lse=None, *, scale: Optional[float] = None,
+                   causal: bool = False, stream=None) -> Tuple["object", "object"]:
+    """O = softmax(scale * Q K^T) V and LSE for contiguous [B, H, N, d] tensors.
+
+    q, k, v: device tensors of one dtype (float32, float16 or bfloat16).
+    o, lse: optional preallocated outputs ([B, H, N, d] of q's dtype and
+    [B, H, N] float32); allocated here when omitted.
+    scale: defaults to 1/sqrt(d).  causal: lower-triangular mask (j <= i).
+    stream: a torch.cuda.Stream; defaults to the current stream of q's device.
+    The kernel is enqueued asynchronously on that stream.
+    """
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise ValueError(f"{name} must be a device tensor")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [B, H, N, d] tensor")
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k and v must have the same shape")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k and v must have the same dtype")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k and v must be on the same device")
+    B, H, N, d = q.shape
+    code = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if o.shape != q.shape or o.dtype != q.dtype or o.device != q.device or not o.is_contiguous():
+        raise ValueError("o must be a contiguous tensor like q")
+    if (lse.shape != (B, H, N) or lse.dtype != torch.float32 or lse.device != q.device
+            or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    L = lib()
+    with torch.cuda.device(q.device):
+        s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        st = L.flash_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              lse.data_ptr(), B, H, N, d, float(scale), int(bool(causal)),
+                              code, s.cuda_stream)
+    if st != 0:
+        raise FlashAttnError(st, L.flash_attn_last_error().decode())
+    return o, lse

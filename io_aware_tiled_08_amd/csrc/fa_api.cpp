@@ -1,0 +1,149 @@
+// C ABI of the gfx950 FlashAttention forward library: argument validation,
+// device checks and dispatch to the kernels.  The contract of every entry
+// point is documented in include/fa_mi355x.h.
+#include "fa_mi355x.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "fa_launch.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+fa_status fail(fa_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
+fa_status fail(fa_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bool overlaps(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + (uintptr_t)b_bytes && b0 < a0 + (uintptr_t)a_bytes;
+}
+
+// Per-device result of the architecture check: 0 unknown, 1 gfx950, 2 other.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_ok[kMaxDevices];
+char g_arch_name[kMaxDevices][64];
+
+fa_status check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0)
+    return fail(FA_ERR_NO_DEVICE, "no usable HIP device: %s", hipGetErrorString(e));
+  if (dev >= kMaxDevices) return fail(FA_ERR_NO_DEVICE, "device index %d too large", dev);
+  int state = g_arch_ok[dev].load(std::memory_order_acquire);
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess)
+      return fail(FA_ERR_NO_DEVICE, "hipGetDeviceProperties(%d): %s", dev, hipGetErrorString(e));
+    // gcnArchName looks like "gfx950:sramecc+:xnack-".
+    std::snprintf(g_arch_name[dev], sizeof(g_arch_name[dev]), "%s", prop.gcnArchName);
+    state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 &&
+                    (prop.gcnArchName[6] == '\0' || prop.gcnArchName[6] == ':')
+                ? 1
+                : 2;
+    g_arch_ok[dev].store(state, std::memory_order_release);
+  }
+  if (state != 1)
+    return fail(FA_ERR_ARCH, "device %d is %s; this library is built for gfx950", dev,
+                g_arch_name[dev]);
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
+                         fa_dtype dtype, void* stream) {
+  g_last_error[0] = '\0';
+  if (!q || !k || !v || !o || !lse) return fail(FA_ERR_NULL, "q, k, v, o and lse must be non-NULL");
+  if (B < 0 || H < 0 || N < 0)
+    return fail(FA_ERR_SHAPE, "B, H, N must be >= 0 (got %lld, %lld, %lld)", (long long)B,
+                (long long)H, (long long)N);
+  if (d != 64 && d != 128) return fail(FA_ERR_HEAD_DIM, "d must be 64 or 128 (got %lld)", (long long)d);
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16)
+    return fail(FA_ERR_DTYPE, "unknown dtype %d", (int)dtype);
+  if (!std::isfinite(scale)) return fail(FA_ERR_SCALE, "scale must be finite");
+  const uintptr_t mis = ((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse) & 15u;
+  if (mis) return fail(FA_ERR_ALIGN, "q, k, v, o and lse must be 16-byte aligned");
+  if (B == 0 || H == 0 || N == 0) return FA_OK;
+
+  // Index math uses int64 element offsets and a 32-bit grid.
+  const int64_t elem = dtype == FA_F32 ? 4 : 2;
+  const int64_t kLimit = (int64_t)1 << 62;
+  if (B > kLimit / H || N > kLimit / (B * H) || d * elem > kLimit / (B * H * N))
+    return fail(FA_ERR_SHAPE, "B*H*N*d*elem overflows");
+  const int64_t BH = B * H;
+  const int br = fa::rows_per_workgroup((fa::Dtype)dtype, (int)d, causal != 0);
+  const int64_t n_qblk = (N + br - 1) / br;
+  if (n_qblk > INT32_MAX || BH * n_qblk > (int64_t)INT32_MAX)
+    return fail(FA_ERR_SHAPE, "B*H*ceil(N/%d) = %lld workgroups exceeds the grid limit", br,
+                (long long)(BH * n_qblk));
+
+  const int64_t tbytes = BH * N * d * elem;
+  const int64_t lbytes = BH * N * 4;
+  if (overlaps(o, tbytes, q, tbytes) || overlaps(o, tbytes, k, tbytes) ||
+      overlaps(o, tbytes, v, tbytes) || overlaps(lse, lbytes, q, tbytes) ||
+      overlaps(lse, lbytes, k, tbytes) || overlaps(lse, lbytes, v, tbytes) ||
+      overlaps(lse, lbytes, o, tbytes))
+    return fail(FA_ERR_ALIAS, "o and lse must not overlap q, k, v or each other");
+
+  fa_status st = check_device();
+  if (st != FA_OK) return st;
+
+  fa::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.BH = BH;
+  a.N = N;
+  a.d = (int)d;
+  a.scale = scale;
+  a.causal = causal != 0;
+  a.dtype = (fa::Dtype)dtype;
+  (void)hipGetLastError();  // do not report an earlier, unrelated error
+  const hipError_t e = fa::launch_forward(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
+const char* flash_attn_status_str(fa_status s) {
+  switch (s) {
+    case FA_OK: return "FA_OK: success";
+    case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: invalid B, H or N";
+    case FA_ERR_HEAD_DIM: return "FA_ERR_HEAD_DIM: unsupported head dimension";
+    case FA_ERR_DTYPE: return "FA_ERR_DTYPE: unknown dtype";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: pointer not 16-byte aligned";
+    case FA_ERR_SCALE: return "FA_ERR_SCALE: scale is not finite";
+    case FA_ERR_ALIAS: return "FA_ERR_ALIAS: output overlaps an input";
+    case FA_ERR_NO_DEVICE: return "FA_ERR_NO_DEVICE: no usable HIP device";
+    case FA_ERR_ARCH: return "FA_ERR_ARCH: device is not gfx950";
+    case FA_ERR_HIP: return "FA_ERR_HIP: HIP runtime error";
+  }
+  return "unknown fa_status";
+}
+
+const char* flash_attn_last_error(void) { return g_last_error; }
+
+int flash_attn_abi_version(void) { return FA_MI355X_ABI_VERSION; }
+
+}  // extern "C"

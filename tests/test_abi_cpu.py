@@ -1,0 +1,153 @@
+"""The C ABI library on a host without a GPU: it loads, exports what the
+header declares, and rejects every bad argument before touching HIP."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa_mi355x.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from io_aware_tiled_08_amd import binding, build
+    if not os.path.exists(binding.library_path()):
+        build.build_library()
+    return binding.lib()
+
+
+def _header():
+    with open(HEADER) as f:
+        return f.read()
+
+
+def test_exports_every_declared_function(L):
+    from io_aware_tiled_08_amd import binding
+    declared = set(re.findall(r"^\s*[A-Za-z_][\w\s\*]*?\b(flash_attn_\w+)\s*\(", _header(), re.M))
+    assert declared == set(binding.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_abi_version_matches_header(L):
+    m = re.search(r"#define\s+FA_MI355X_ABI_VERSION\s+(\d+)", _header())
+    assert int(m.group(1)) == L.flash_attn_abi_version()
+
+
+def test_status_codes_match_header(L):
+    from io_aware_tiled_08_amd import binding
+    enum = dict((name, int(val)) for name, val in
+                re.findall(r"\b(FA_(?:OK|ERR_\w+))\s*=\s*(\d+)", _header()))
+    assert enum == binding.STATUS_CODE
+    texts = {L.flash_attn_status_str(c).decode() for c in enum.values()}
+    assert len(texts) == len(enum)
+    for name, code in enum.items():
+        assert L.flash_attn_status_str(code).decode().startswith(name)
+    assert L.flash_attn_status_str(999).decode() == "unknown fa_status"
+    dt = dict(re.findall(r"\b(FA_(?:F32|F16|BF16))\s*=\s*(\d+)", _header()))
+    assert {k: int(v) for k, v in dt.items()} == {
+        "FA_F32": binding.FA_F32, "FA_F16": binding.FA_F16, "FA_BF16": binding.FA_BF16}
+
+
+# Fake, 16-byte aligned, non-overlapping device addresses: every call below
+# returns before anything could dereference them.
+GiB = 1 << 30
+Q, K, V, O, LSE = (0x10000000000 + i * 64 * GiB for i in range(5))
+
+
+def _call(L, q=Q, k=K, v=V, o=O, lse=LSE, B=2, H=3, N=100, d=64, scale=0.125,
+          causal=0, dtype=1):
+    st = L.flash_attn_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, None)
+    return st, L.flash_attn_last_error().decode()
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "o", "lse"])
+def test_null_pointer(L, field):
+    st, msg = _call(L, **{field: None})
+    assert st == 1 and "non-NULL" in msg
+
+
+@pytest.mark.parametrize("shape", [(-1, 1, 1), (1, -2, 1), (1, 1, -3)])
+def test_negative_shape(L, shape):
+    B, H, N = shape
+    assert _call(L, B=B, H=H, N=N)[0] == 2
+
+
+def test_overflowing_shape(L):
+    assert _call(L, B=1 << 40, H=1 << 20, N=1 << 10)[0] == 2
+
+
+def test_grid_limit(L):
+    # 2^31 query blocks cannot be launched on a 32-bit grid.
+    assert _call(L, B=1 << 20, H=1 << 11, N=1 << 10)[0] == 2
+
+
+@pytest.mark.parametrize("d", [0, 32, 96, 100, 256, -64])
+def test_head_dim(L, d):
+    assert _call(L, d=d)[0] == 3
+
+
+@pytest.mark.parametrize("dtype", [-1, 3, 42])
+def test_dtype(L, dtype):
+    assert _call(L, dtype=dtype)[0] == 4
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "o", "lse"])
+def test_misaligned(L, field):
+    base = {"q": Q, "k": K, "v": V, "o": O, "lse": LSE}[field]
+    assert _call(L, **{field: base + 8})[0] == 5
+
+
+@pytest.mark.parametrize("scale", [math.nan, math.inf, -math.inf])
+def test_scale(L, scale):
+    assert _call(L, scale=scale)[0] == 6
+
+
+@pytest.mark.parametrize("o,lse", [(Q, LSE), (K + 4096, LSE), (O, V + 256), (O, O + 1024)])
+def test_alias(L, o, lse):
+    assert _call(L, o=o, lse=lse)[0] == 7
+
+
+def test_inputs_may_alias_each_other(L):
+    st, _ = _call(L, k=Q, v=Q)
+    assert st != 7
+
+
+@pytest.mark.parametrize("shape", [(0, 3, 100), (2, 0, 100), (2, 3, 0)])
+def test_empty_is_a_no_op(L, shape):
+    B, H, N = shape
+    assert _call(L, B=B, H=H, N=N) == (0, "")
+
+
+def test_no_device_reported_not_crashed(L):
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    st, msg = _call(L)
+    assert st == 8, msg
+    assert msg
+
+
+def test_error_string_cleared_on_success(L):
+    assert _call(L, d=96)[0] == 3
+    assert L.flash_attn_last_error().decode() != ""
+    assert _call(L, N=0) == (0, "")
+
+
+def test_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    from io_aware_tiled_08_amd import flash_attn_fwd
+    x = torch.zeros(1, 1, 4, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        flash_attn_fwd(x, x, x)
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    from io_aware_tiled_08_amd import binding
+    monkeypatch.setenv("FA_MI355X_LIB", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(binding, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        binding.lib()

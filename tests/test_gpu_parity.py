@@ -1,0 +1,183 @@
+"""HIP path vs the fp64 oracle on identical seeded inputs (needs a gfx950 GPU).
+
+Tolerances: max-abs error against fp64 of 2e-3 for fp16, 1e-2 for bf16 and
+1e-5 for fp32 inputs, applied to O and to LSE alike.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from io_aware_tiled_08_amd import FlashAttnError, flash_attn_fwd
+from io_aware_tiled_08_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "f16": 2e-3, "bf16": 1e-2}
+DEV = "cuda:0"
+
+
+def gpu_forward(q, k, v, scale, causal, stream=None):
+    """Runs the kernel with O and LSE pre-filled with NaN, so any element the
+    kernel fails to write shows up."""
+    qd, kd, vd = (x.to(DEV) for x in (q, k, v))
+    o = torch.full_like(qd, float("nan"))
+    lse = torch.full(tuple(q.shape[:3]), float("nan"), dtype=torch.float32, device=DEV)
+    flash_attn_fwd(qd, kd, vd, o, lse, scale=scale, causal=causal, stream=stream)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def check(o, lse, q, k, v, scale, causal, dtype, rows=None, label=""):
+    O_ref, L_ref = oracle.attention_forward(q, k, v, scale, causal, rows=rows)
+    O = o.double().cpu().numpy()
+    L = lse.double().cpu().numpy()
+    if rows is not None:
+        O = np.take_along_axis(O, rows[..., None], axis=2)
+        L = np.take_along_axis(L, rows, axis=2)
+    assert np.isfinite(O).all() and np.isfinite(L).all(), f"{label}: non-finite output"
+    err_o = float(np.max(np.abs(O - O_ref))) if O.size else 0.0
+    err_l = float(np.max(np.abs(L - L_ref))) if L.size else 0.0
+    print(f"{label}: max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}", flush=True)
+    assert err_o <= TOL[dtype], f"{label}: O error {err_o:.3e} > {TOL[dtype]}"
+    assert err_l <= TOL[dtype], f"{label}: LSE error {err_l:.3e} > {TOL[dtype]}"
+    return err_o, err_l
+
+
+SWEEP_N = [1, 2, 17, 63, 64, 65, 127, 128, 129, 255, 256, 257, 300, 1000]
+
+
+@pytest.mark.parametrize("N", SWEEP_N)
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
+def test_sweep(dtype, d, causal, N):
+    q, k, v = W.random_qkv(1, 2, N, d, dtype, seed=1000 + N)
+    scale = W.default_scale(d)
+    o, lse = gpu_forward(q, k, v, scale, causal)
+    check(o, lse, q, k, v, scale, causal, dtype, label=f"{dtype} d={d} causal={causal} N={N}")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
+def test_batch_and_head_indexing(dtype):
+    q, k, v = W.random_qkv(3, 5, 100, 64, dtype, seed=77)
+    for causal in (False, True):
+        o, lse = gpu_forward(q, k, v, 0.125, causal)
+        check(o, lse, q, k, v, 0.125, causal, dtype, label=f"B3H5 {dtype} causal={causal}")
+
+
+@pytest.mark.parametrize("scale", [-0.2, 0.0, 1.5])
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
+def test_unusual_scales(dtype, scale):
+    q, k, v = W.random_qkv(1, 2, 200, 128, dtype, seed=5)
+    for causal in (False, True):
+        o, lse = gpu_forward(q, k, v, scale, causal)
+        check(o, lse, q, k, v, scale, causal, dtype,
+              label=f"{dtype} scale={scale} causal={causal}")
+
+
+def test_rescale_stress_small():
+    """Growing score maxima along the sequence (the rescale-stress recipe at a
+    size the oracle handles whole)."""
+    q, k, v = W.random_qkv(1, 4, 3000, 128, "bf16", seed=44, kind="rescale_stress")
+    o, lse = gpu_forward(q, k, v, W.default_scale(128), True)
+    check(o, lse, q, k, v, W.default_scale(128), True, "bf16", label="stress bf16 N=3000")
+    q, k, v = W.random_qkv(1, 4, 3000, 64, "f16", seed=45, kind="rescale_stress")
+    o, lse = gpu_forward(q, k, v, W.default_scale(64), True)
+    check(o, lse, q, k, v, W.default_scale(64), True, "f16", label="stress f16 N=3000")
+
+
+def test_constant_v_and_dominant_key():
+    N, d = 333, 64
+    q, k, _ = W.random_qkv(1, 1, N, d, "f16", seed=9)
+    v = torch.full((1, 1, N, d), 0.75, dtype=torch.float16)
+    o, _ = gpu_forward(q, k, v, 0.125, False)
+    assert torch.all(o.float().cpu() == 0.75)
+    # One key aligned with every query by a wide margin: O is that key's V row.
+    q = torch.zeros(1, 1, N, d, dtype=torch.float16)
+    q[..., 0] = 1.0
+    k = torch.zeros(1, 1, N, d, dtype=torch.float16)
+    k[0, 0, 200, 0] = 60.0
+    v = torch.randn(1, 1, N, d).to(torch.float16)
+    o, lse = gpu_forward(q, k, v, 1.0, False)
+    assert torch.allclose(o[0, 0].float().cpu(), v[0, 0, 200].float().expand(N, d), atol=1e-3)
+    assert torch.allclose(lse.cpu(), torch.full((1, 1, N), 60.0), atol=1e-3)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
+def test_deterministic(dtype):
+    q, k, v = W.random_qkv(2, 2, 777, 128, dtype, seed=3)
+    o1, l1 = gpu_forward(q, k, v, 0.09, True)
+    o2, l2 = gpu_forward(q, k, v, 0.09, True)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_side_stream():
+    q, k, v = W.random_qkv(1, 2, 500, 64, "f16", seed=8)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o, lse = gpu_forward(q, k, v, 0.125, True, stream=s)
+    check(o, lse, q, k, v, 0.125, True, "f16", label="side stream")
+
+
+def test_misaligned_pointer_is_rejected():
+    x = torch.zeros(4 * 64 + 1, dtype=torch.float16, device=DEV)
+    q = x[1:].view(1, 1, 4, 64)
+    with pytest.raises(FlashAttnError, match="FA_ERR_ALIGN"):
+        flash_attn_fwd(q, q, q)
+
+
+def test_bad_head_dim_is_rejected():
+    x = torch.zeros(1, 1, 4, 96, dtype=torch.float16, device=DEV)
+    with pytest.raises(FlashAttnError, match="FA_ERR_HEAD_DIM"):
+        flash_attn_fwd(x, x, x)
+
+
+def test_empty_sequence():
+    x = torch.zeros(1, 2, 0, 64, dtype=torch.float16, device=DEV)
+    o, lse = flash_attn_fwd(x, x, x)
+    assert o.shape == x.shape and lse.shape == (1, 2, 0)
+
+
+# --- the named workloads, in the launch configuration the benchmark times ---
+
+def _boundary_rows(N, count, seed):
+    """Sampled query rows plus the first/last rows and rows around every
+    1024-row boundary."""
+    base = set(range(0, min(N, 4))) | set(range(max(0, N - 4), N))
+    for b in range(0, N, 1024):
+        base |= {x for x in (b - 1, b, b + 1) if 0 <= x < N}
+    rng = np.random.default_rng([seed, 99])
+    rest = rng.choice(N, size=min(N, count), replace=False)
+    return np.array(sorted(base | set(int(x) for x in rest)), dtype=np.int64)
+
+
+def _run_workload(name, rows=None):
+    w = W.WORKLOADS[name]
+    q, k, v = W.workload_inputs(w)
+    print(f"workload {name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype} causal={w.causal}",
+          flush=True)
+    o, lse = gpu_forward(q, k, v, w.scale, w.causal)
+    return w, q, k, v, o, lse
+
+
+@pytest.mark.parametrize("name", ["single_head_f32", "batch_f16_d64", "batch_f16_d64_causal"])
+def test_workload_full(name):
+    w, q, k, v, o, lse = _run_workload(name)
+    check(o, lse, q, k, v, w.scale, w.causal, w.dtype, label=name)
+
+
+@pytest.mark.parametrize("name", ["headline_f16_d128", "rescale_stress_bf16"])
+def test_workload_sampled(name):
+    w, q, k, v, o, lse = _run_workload(name)
+    rows = _boundary_rows(w.N, 256, w.seed)
+    check(o, lse, q, k, v, w.scale, w.causal, w.dtype, rows=rows, label=name)
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
+def test_workload_long_context():
+    name = "long_context_bf16"
+    w, q, k, v, o, lse = _run_workload(name)
+    rows = W.sample_rows(w.seed, w.B, w.H, w.N, w.sampled_rows)
+    check(o, lse, q, k, v, w.scale, w.causal, w.dtype, rows=rows, label=name)
+    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
