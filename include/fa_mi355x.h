@@ -68,7 +68,8 @@ typedef enum {
  *            overwritten (rounded to nearest even from fp32).
  *   lse      device pointer, contiguous [B, H, N] float32; fully overwritten.
  *   B, H, N  batch, heads and sequence length, each >= 0.  If any is 0 the
- *            call returns FA_OK without touching the device.
+ *            call returns FA_OK once d, dtype and scale are checked, without
+ *            looking at any pointer (they may be NULL) or touching the device.
  *   d        head dimension: 64 or 128.
  *   scale    finite float multiplying Q K^T (usually 1/sqrt(d)); negative and
  *            zero values are allowed.

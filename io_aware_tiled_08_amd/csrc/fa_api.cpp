@@ -72,7 +72,6 @@ fa_status flash_attn_fwd(const void* q, const void* k, const void* v, void* o, f
                          int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
                          fa_dtype dtype, void* stream) {
   g_last_error[0] = '\0';
-  if (!q || !k || !v || !o || !lse) return fail(FA_ERR_NULL, "q, k, v, o and lse must be non-NULL");
   if (B < 0 || H < 0 || N < 0)
     return fail(FA_ERR_SHAPE, "B, H, N must be >= 0 (got %lld, %lld, %lld)", (long long)B,
                 (long long)H, (long long)N);
@@ -80,9 +79,11 @@ fa_status flash_attn_fwd(const void* q, const void* k, const void* v, void* o, f
   if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16)
     return fail(FA_ERR_DTYPE, "unknown dtype %d", (int)dtype);
   if (!std::isfinite(scale)) return fail(FA_ERR_SCALE, "scale must be finite");
+  // An empty problem reads no pointer (zero-size buffers may be NULL).
+  if (B == 0 || H == 0 || N == 0) return FA_OK;
+  if (!q || !k || !v || !o || !lse) return fail(FA_ERR_NULL, "q, k, v, o and lse must be non-NULL");
   const uintptr_t mis = ((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse) & 15u;
   if (mis) return fail(FA_ERR_ALIGN, "q, k, v, o and lse must be 16-byte aligned");
-  if (B == 0 || H == 0 || N == 0) return FA_OK;
 
   // Index math uses int64 element offsets and a 32-bit grid.
   const int64_t elem = dtype == FA_F32 ? 4 : 2;

@@ -120,6 +120,8 @@ def test_inputs_may_alias_each_other(L):
 def test_empty_is_a_no_op(L, shape):
     B, H, N = shape
     assert _call(L, B=B, H=H, N=N) == (0, "")
+    assert _call(L, q=None, o=None, lse=None, B=B, H=H, N=N) == (0, "")
+    assert _call(L, B=B, H=H, N=N, d=96)[0] == 3
 
 
 def test_no_device_reported_not_crashed(L):
