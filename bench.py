@@ -22,7 +22,7 @@ if ROOT not in sys.path:
 # MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s).
 MFMA_PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3}
 HBM_PEAK_GBPS = 8000.0
-KERNEL_SOURCE = os.path.join(ROOT, "io_aware_tiled_08_amd", "csrc", "fa_fwd_kernel.hip")
+KERNEL_SOURCE = os.path.join(ROOT, "io_aware_tiled_08_amd", "csrc", "fa_fwd_f16.hip")
 PROFILES = os.path.join(ROOT, "profiles")
 
 

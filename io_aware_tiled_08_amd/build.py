@@ -18,6 +18,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libfa_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
+KERNEL_SOURCES = ("fa_fwd_f16.hip", "fa_fwd_f32.hip")
 
 
 def hipcc() -> str:
@@ -44,14 +45,17 @@ def build_library(verbose: bool = False, extra_flags=()) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     cc = hipcc()
     common = ["-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC, *extra_flags]
-    kobj = os.path.join(BUILD_DIR, "fa_fwd_kernel.o")
+    objs = []
+    for src in KERNEL_SOURCES:
+        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        _run([cc, f"--offload-arch={ARCH}", *common,
+              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+              "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
     aobj = os.path.join(BUILD_DIR, "fa_api.o")
-    _run([cc, f"--offload-arch={ARCH}", *common,
-          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-c", os.path.join(CSRC, "fa_fwd_kernel.hip"), "-o", kobj], verbose)
     _run([cc, *common, "-Wall", "-c", os.path.join(CSRC, "fa_api.cpp"), "-o", aobj], verbose)
     tmp = LIB_PATH + ".tmp"
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", kobj, aobj, "-o", tmp], verbose)
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, aobj, "-o", tmp], verbose)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

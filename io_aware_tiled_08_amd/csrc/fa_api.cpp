@@ -91,7 +91,7 @@ fa_status flash_attn_fwd(const void* q, const void* k, const void* v, void* o, f
   if (B > kLimit / H || N > kLimit / (B * H) || d * elem > kLimit / (B * H * N))
     return fail(FA_ERR_SHAPE, "B*H*N*d*elem overflows");
   const int64_t BH = B * H;
-  const int br = fa::rows_per_workgroup((fa::Dtype)dtype, (int)d, causal != 0);
+  const int br = fa::rows_per_workgroup((fa::Dtype)dtype);
   const int64_t n_qblk = (N + br - 1) / br;
   if (n_qblk > INT32_MAX || BH * n_qblk > (int64_t)INT32_MAX)
     return fail(FA_ERR_SHAPE, "B*H*ceil(N/%d) = %lld workgroups exceeds the grid limit", br,
@@ -121,7 +121,8 @@ fa_status flash_attn_fwd(const void* q, const void* k, const void* v, void* o, f
   a.causal = causal != 0;
   a.dtype = (fa::Dtype)dtype;
   (void)hipGetLastError();  // do not report an earlier, unrelated error
-  const hipError_t e = fa::launch_forward(a, (hipStream_t)stream);
+  const hipError_t e = dtype == FA_F32 ? fa::launch_forward_f32(a, (hipStream_t)stream)
+                                       : fa::launch_forward_f16(a, (hipStream_t)stream);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return FA_OK;
 }

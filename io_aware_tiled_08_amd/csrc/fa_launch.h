@@ -1,5 +1,6 @@
 // Internal interface between the C ABI layer (fa_api.cpp) and the gfx950
-// kernels (fa_fwd_kernel.hip).  Not installed, not part of the ABI.
+// kernels (fa_fwd_f16.hip, fa_fwd_f32.hip).  Not installed, not part of the
+// ABI.
 #pragma once
 
 #include <hip/hip_runtime_api.h>
@@ -15,7 +16,7 @@ struct FwdArgs {
   const void* v;
   void* o;
   float* lse;
-  int64_t BH;      // B * H
+  int64_t BH;  // B * H
   int64_t N;
   int d;
   float scale;
@@ -23,11 +24,16 @@ struct FwdArgs {
   Dtype dtype;
 };
 
-// Rows of Q owned by one workgroup for a (dtype, d, causal) choice; the
-// caller uses it for the grid-size overflow check.
-int rows_per_workgroup(Dtype dtype, int d, bool causal);
+// Query rows owned by one workgroup (fixes the grid size).
+constexpr int kRowsPerWorkgroupF16 = 256;
+constexpr int kRowsPerWorkgroupF32 = 64;
 
-// Enqueue the forward kernel on `stream`.  Arguments are already validated.
-hipError_t launch_forward(const FwdArgs& a, hipStream_t stream);
+inline int rows_per_workgroup(Dtype dtype) {
+  return dtype == Dtype::F32 ? kRowsPerWorkgroupF32 : kRowsPerWorkgroupF16;
+}
+
+// Enqueue the forward kernel on `stream`; arguments are already validated.
+hipError_t launch_forward_f16(const FwdArgs& a, hipStream_t stream);  // FA_F16, FA_BF16
+hipError_t launch_forward_f32(const FwdArgs& a, hipStream_t stream);
 
 }  // namespace fa
