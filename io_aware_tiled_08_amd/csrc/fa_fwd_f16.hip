@@ -15,13 +15,21 @@
 //     was accumulated is multiplied by exp(m_old - m_new).
 //
 // CDNA4 mapping (our design, not the pages'):
-//   * Workgroup = 8 waves x 32 query rows.  At <= 256 VGPRs per wave two waves
-//     share a SIMD, so one wave's softmax (VALU) runs under the other wave's
-//     matrix products (MFMA).
-//   * K and V tiles (64 keys) are double buffered in LDS, row-major, with the
-//     16-byte chunks of each row permuted (XOR swizzle) so that the reads below
-//     hit all LDS banks; the next tile's global loads are in flight while the
-//     current tile is consumed.
+//   * Workgroup = 8 waves x 32 query rows, in two groups of four (waves 0-3
+//     and 4-7; wave w runs on SIMD w % 4, so every SIMD holds one wave of each
+//     group).  The groups run half a tile apart ("ping-pong"): while one group
+//     issues matrix products (M phase) the other runs the softmax on the
+//     vector ALU (V phase), and a workgroup barrier swaps the roles.  For the
+//     tile t a wave's M phase is  O += P(t-1) V(t-1)  followed by  S(t) =
+//     K(t) Q^T, and its V phase turns S(t) into P(t).  The M-phase wave runs
+//     at raised priority so its matrix instructions issue first.
+//   * K and V tiles (64 keys) are double buffered in LDS and filled by
+//     buffer_load ... lds (HBM/L2 straight into LDS, no register staging).
+//     Each row's 16-byte chunks are stored XOR-permuted so that the operand
+//     reads hit all LDS banks; the permutation is applied on the global side
+//     (lane i of a load always writes LDS bytes 16i..16i+15).  Loads for tile
+//     t+1 are issued one tile ahead and only waited for at the barrier before
+//     their first use.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_{f16,bf16}: a lane owns one query
 //     (accumulator column) and 16 keys, the other 16 sit in lane l^32, so the
 //     row max and sum are in-lane plus one v_permlane32_swap, and the rescale
@@ -46,6 +54,8 @@ namespace {
 // fp16/bf16 range and exact-ratio in fp32.
 constexpr float kRescaleSlack = 8.0f;
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
 template <typename T>
 struct Half;
 
@@ -56,11 +66,9 @@ struct Half<_Float16> {
   static __device__ __forceinline__ f32x16 mma(Frag a, Frag b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
   }
+  // Round-to-nearest-even pair conversion (v_cvt_pk_f16_f32).
   static __device__ __forceinline__ Pair pack(float x, float y) {
-    Pair p;
-    p[0] = (_Float16)x;
-    p[1] = (_Float16)y;
-    return p;
+    return __builtin_convertvector((f32x2){x, y}, Pair);
   }
   // acc + p.x + p.y in fp32 (v_dot2 with ones)
   static __device__ __forceinline__ float sum2(Pair p, float acc) {
@@ -76,11 +84,9 @@ struct Half<__bf16> {
   static __device__ __forceinline__ f32x16 mma(Frag a, Frag b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
+  // Round-to-nearest-even pair conversion (v_cvt_pk_bf16_f32).
   static __device__ __forceinline__ Pair pack(float x, float y) {
-    Pair p;
-    p[0] = (__bf16)x;
-    p[1] = (__bf16)y;
-    return p;
+    return __builtin_convertvector((f32x2){x, y}, Pair);
   }
   static __device__ __forceinline__ float sum2(Pair p, float acc) {
     const Pair one = {(__bf16)1.0f, (__bf16)1.0f};
@@ -89,7 +95,8 @@ struct Half<__bf16> {
 };
 
 // Position of 16-byte chunk c of row r inside the LDS row (rows are 2*D bytes,
-// LDS banks repeat every 256 bytes = 16 chunks).
+// LDS banks repeat every 256 bytes = 16 chunks).  Each map is an XOR with a
+// row-dependent mask, so it is its own inverse.
 //   K is read as MFMA A rows: 16 lanes read one chunk of 16 different rows
 //   (rows distinct mod 16), so those must land in 16 different bank groups.
 //   V is read by transposing loads: 32 lanes read 4 chunks of 4 consecutive
@@ -108,6 +115,7 @@ struct Swizzle {
 typedef short s16x4 __attribute__((vector_size(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) void lds_void;
 
 // ds_read_b64_tr_b16: within each group of 16 lanes, output lane i, element
 // e receives element i%4 of the 4 elements addressed by lane 4*e + i/4.  When
@@ -119,31 +127,61 @@ __device__ __forceinline__ u32x2 lds_read_tr(const char* base, int byte_off) {
   return bits<u32x2>(__builtin_amdgcn_ds_read_tr16_b64_v4i16(ptr));
 }
 
-template <typename T, int D, bool CAUSAL, int NW, int BC>
-__global__ void __launch_bounds__(NW * 64, 1) fwd_f16_kernel(KernelParams p) {
+// Raw buffer resource over [base, base + bytes): buffer loads at offsets
+// >= bytes return zeros.  Dword 3 is the gfx9 raw-buffer format word.
+__device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+
+// buffer_load_dwordx4 ... lds: lane i copies the 16 bytes at buffer offset
+// voff into LDS bytes lds + 16*i .. +15.  Issued from inline assembly so that
+// the compiler's wait-count pass does not make every later LDS read wait for
+// these loads (it cannot tell the double buffers apart); the kernel waits for
+// them itself (vmcnt(0) + barrier) before the first read of the buffer.  M0
+// holds the LDS base; nothing else in these kernels uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma_load16(u32x4 rsrc, uint32_t lds, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_char*)const_cast<void*>(p);
+}
+
+template <typename T, int D, bool CAUSAL>
+__global__ void __launch_bounds__(512, 1) fwd_f16_kernel(KernelParams p) {
   using H = Half<T>;
   using Frag = typename H::Frag;
   using Pair = typename H::Pair;
   using Sw = Swizzle<D>;
-  constexpr int NT = NW * 64;        // threads per workgroup
+  constexpr int NW = 8;              // waves per workgroup
   constexpr int BR = NW * 32;        // query rows per workgroup
+  constexpr int BC = 64;             // keys per tile
   constexpr int RB = D * 2;          // bytes per row of K or V
   constexpr int CPR = D / 8;         // 16-byte chunks per row
   constexpr int TILE = BC * RB;      // bytes of one staged K (or V) tile
   constexpr int NKB = BC / 32;       // 32-key blocks per tile
   constexpr int NKS = D / 16;        // MFMAs per 32x32 score block
   constexpr int ND = D / 32;         // 32-row blocks of O^T
-  constexpr int CHUNKS = BC * CPR;   // 16-byte chunks per staged tile
-  constexpr int ITERS = CHUNKS / NT;
-  static_assert(CHUNKS % NT == 0 && BC % 32 == 0, "tile shape");
+  constexpr int RPL = 1024 / RB;     // rows one wave-wide 1 KiB load covers
+  constexpr int LPW = TILE / 1024 / 4;  // 1 KiB loads per loading wave per tensor
+  static_assert(LPW >= 1 && TILE % 4096 == 0, "tile shape");
 
-  __shared__ __attribute__((aligned(16))) char smem[2][2][TILE];  // [buffer][K, V]
+  __shared__ __attribute__((aligned(1024))) char smem[2][2][TILE];  // [K, V][buffer]
 
   const WorkItem wi = work_item<CAUSAL>(p.n_qblk);
   const int64_t N = p.N;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool group_b = wave >= 4;
+  const int gw = wave & 3;  // wave index inside its group
   const int l32 = lane & 31;
   const int hh = lane >> 5;
   const int64_t q0 = (int64_t)wi.qblk * BR;
@@ -155,6 +193,52 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_f16_kernel(KernelParams p) {
   const T* __restrict__ Vh = (const T*)p.v + wi.bh * N * D;
   T* __restrict__ Oh = (T*)p.o + wi.bh * N * D;
   float* __restrict__ Lh = p.lse + wi.bh * N;
+
+  const int64_t kv_end = CAUSAL ? (q0 + BR < N ? q0 + BR : N) : N;
+  const int n_tiles = (int)((kv_end + BC - 1) / BC);
+  const int64_t wave_end = CAUSAL ? (qw + 32 < N ? qw + 32 : N) : N;
+  const int wave_tiles = qw < N ? (int)((wave_end + BC - 1) / BC) : 0;
+
+  // ---- tile loads: global -> LDS, 16 bytes per lane -------------------------
+  // Group A (four waves) loads every tile.  Load j of group-wave gw
+  // covers rows (gw*LPW + j)*RPL .. +RPL of the tile; lane i fills LDS chunk
+  // slot i%CPR of row .. + i/CPR, which holds global chunk slot ^ mask(row).
+  int kvoff[LPW], vvoff[LPW];
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int r = (gw * LPW + j) * RPL + lane / CPR;
+    const int slot = lane % CPR;
+    kvoff[j] = r * RB + Sw::k(r, slot) * 16;
+    vvoff[j] = r * RB + Sw::v(r, slot) * 16;
+  }
+  const uint32_t lds_k = lds_addr(&smem[0][0][0]) + gw * LPW * 1024;
+  const uint32_t lds_v = lds_addr(&smem[1][0][0]) + gw * LPW * 1024;
+  auto issue_k = [&](int t) {
+    if (t >= n_tiles) return;
+    const int64_t k0 = (int64_t)t * BC;
+    const uint32_t rows = (uint32_t)(N - k0 < BC ? N - k0 : BC);
+    const u32x4 rs = buffer_rsrc(Kh + k0 * D, rows * RB);
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) dma_load16(rs, lds_k + (t & 1) * TILE + j * 1024, kvoff[j]);
+  };
+  auto issue_v = [&](int t) {
+    if (t >= n_tiles) return;
+    const int64_t k0 = (int64_t)t * BC;
+    const uint32_t rows = (uint32_t)(N - k0 < BC ? N - k0 : BC);
+    const u32x4 rs = buffer_rsrc(Vh + k0 * D, rows * RB);
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) dma_load16(rs, lds_v + (t & 1) * TILE + j * 1024, vvoff[j]);
+  };
+  auto barrier = [] {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto wait_loads = [] {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads have landed in LDS
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
   // Q (B operand of S^T = K Q^T): lane holds Q[qrow][16*ks + 8*hh .. +7].
   Frag qf[NKS];
@@ -168,34 +252,9 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_f16_kernel(KernelParams p) {
       qf[ks] = bits<Frag>(raw);
     }
   }
+  if (!group_b) issue_k(0);
 
-  // ---- staging: global -> registers -> swizzled LDS -------------------------
-  u32x4 kreg[ITERS], vreg[ITERS];
-  // Rows past N read row N-1 (in bounds) and become zeros, so an invisible
-  // key has finite V and a zero weight.
-  auto load_row = [&](const T* base, int64_t g, int c) -> u32x4 {
-    const u32x4 x = *(const u32x4*)(base + (g < N ? g : N - 1) * D + c * 8);
-    return g < N ? x : u32x4{0, 0, 0, 0};
-  };
-  auto load_tile = [&](int64_t k0) {
-#pragma unroll
-    for (int i = 0; i < ITERS; ++i) {
-      const int ch = tid + i * NT;
-      kreg[i] = load_row(Kh, k0 + ch / CPR, ch % CPR);
-      vreg[i] = load_row(Vh, k0 + ch / CPR, ch % CPR);
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < ITERS; ++i) {
-      const int ch = tid + i * NT;
-      const int r = ch / CPR, c = ch % CPR;
-      *(u32x4*)(&smem[buf][0][r * RB + Sw::k(r, c) * 16]) = kreg[i];
-      *(u32x4*)(&smem[buf][1][r * RB + Sw::v(r, c) * 16]) = vreg[i];
-    }
-  };
-
-  // ---- lane-constant LDS offsets --------------------------------------------
+  // ---- lane-constant LDS read offsets ----------------------------------------
   // K A operand for MFMA ks of key block kb: row kb*32 + krow, chunk 2*ks + hh
   // (the swizzle only sees the row modulo 16, so kb does not change it).
   const int krow = k_row_of_lane(l32);
@@ -220,102 +279,17 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_f16_kernel(KernelParams p) {
   f32x16 o[ND];
 #pragma unroll
   for (int db = 0; db < ND; ++db) o[db] = f32x16{};
+  f32x16 s[NKB];
+  Frag pf[NKB][2];
   float m = kNegInf;  // reference maximum of the row, log2 units
   float l = 0.f;      // this lane's share of the row sum (keys it holds)
-
-  const int64_t kv_end = CAUSAL ? (q0 + BR < N ? q0 + BR : N) : N;
-  const int n_tiles = (int)((kv_end + BC - 1) / BC);
-  const int64_t wave_end = CAUSAL ? (qw + 32 < N ? qw + 32 : N) : N;
-  const int wave_tiles = qw < N ? (int)((wave_end + BC - 1) / BC) : 0;
   const float c = p.c;
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    const int64_t k0 = (int64_t)t * BC;
-    if (t + 1 < n_tiles) load_tile(k0 + BC);
-
-    if (t < wave_tiles) {
-      const char* kl = &smem[buf][0][0];
-      const char* vl = &smem[buf][1][0];
-
-      // S^T = K Q^T: s[kb] is keys kb*32.. x this wave's 32 queries.
-      f32x16 s[NKB];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const Frag a = bits<Frag>(*(const u32x4*)(kl + kb * 32 * RB + koff[ks]));
-          s[kb] = H::mma(a, qf[ks], s[kb]);
-        }
-
-      // Invisible keys (past N, or after the query when causal) -> -inf.
-      const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > qw);
-      float mx = kNegInf;
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int64_t key = k0 + kb * 32 + key_of_reg(r, hh);
-            if (key >= N || (CAUSAL && key > qrow)) s[kb][r] = kNegInf;
-            mx = fmaxf(mx, s[kb][r]);
-          }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-      }
-      mx = halves_max(mx);
-      const float mxc = mx == kNegInf ? kNegInf : mx * c;
-
-      // Online softmax: raise the reference maximum (and rescale l and O by
-      // exp2(m_old - m_new)) only when this tile exceeds it by the slack.
-      // m = -inf means no visible key yet: any visible key raises it.
-      const bool grow = mxc > m + kRescaleSlack;
-      if (__ballot(grow)) {
-        const float alpha = grow ? __builtin_amdgcn_exp2f(m - mxc) : 1.0f;
-        m = grow ? mxc : m;
-        l *= alpha;
-#pragma unroll
-        for (int db = 0; db < ND; ++db) o[db] *= alpha;
-      }
-      const float m_use = m == kNegInf ? 0.f : m;
-
-      // P = exp2(c*s - m), rounded to T; l accumulates the rounded weights so
-      // that O's normalisation matches the weights P V actually used.
-      Frag pf[NKB][2];
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          Frag f;
-#pragma unroll
-          for (int i = 0; i < 8; i += 2) {
-            float e[2];
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-              const float x = s[kb][8 * jj + i + u];
-              e[u] = __builtin_amdgcn_exp2f(__builtin_fmaf(x, c, -m_use));
-              if (need_mask && x == kNegInf) e[u] = 0.f;
-            }
-            const Pair pr = H::pack(e[0], e[1]);
-            rs = H::sum2(pr, rs);
-            f[i] = pr[0];
-            f[i + 1] = pr[1];
-          }
-          pf[kb][jj] = f;
-        }
-      l += rs;
-
-      // O^T += V^T P^T.
+  // M phase of tile t: O += P(t-1) V(t-1), then S(t) = K(t) Q^T.
+  auto m_phase = [&](int t) {
+    __builtin_amdgcn_s_setprio(1);
+    if (t >= 1 && t - 1 < wave_tiles) {
+      const char* vl = &smem[1][(t - 1) & 1][0];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -329,10 +303,112 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_f16_kernel(KernelParams p) {
             o[db] = H::mma(a, pf[kb][jj], o[db]);
           }
     }
+    if (t < wave_tiles) {
+      const char* kl = &smem[0][t & 1][0];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const Frag a = bits<Frag>(*(const u32x4*)(kl + kb * 32 * RB + koff[ks]));
+          s[kb] = H::mma(a, qf[ks], s[kb]);
+        }
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
 
-    if (t + 1 < n_tiles) store_tile(buf ^ 1);
-    __syncthreads();
+  // V phase of tile t: online softmax of S(t) into P(t).
+  auto v_phase = [&](int t) {
+    if (t >= wave_tiles) return;
+    const int64_t k0 = (int64_t)t * BC;
+    // Keys k0 + i with i >= lim are invisible (past N, or after the query
+    // when causal): their scores become -inf.  Register r of key block kb
+    // holds key kb*32 + key_of_reg(r, hh) of the tile.
+    int64_t lim64 = N - k0;
+    if (CAUSAL && qrow + 1 - k0 < lim64) lim64 = qrow + 1 - k0;
+    const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > qw);
+    float mx = kNegInf;
+    if (need_mask) {
+      const int lim = (int)(lim64 < 0 ? 0 : (lim64 > BC ? BC : lim64)) - 8 * hh;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if (kb * 32 + key_of_reg(r, 0) >= lim) s[kb][r] = kNegInf;
+          mx = fmaxf(mx, s[kb][r]);
+        }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    }
+    mx = halves_max(mx);
+    const float mxc = mx * c;  // c > 0, so -inf stays -inf
+
+    // Online softmax: raise the reference maximum (and rescale l and O by
+    // exp2(m_old - m_new)) only when this tile exceeds it by the slack.
+    // m = -inf means no visible key yet: any visible key raises it.
+    const bool grow = mxc > m + kRescaleSlack;
+    if (__ballot(grow)) {
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m - mxc) : 1.0f;
+      m = grow ? mxc : m;
+      l *= alpha;
+#pragma unroll
+      for (int db = 0; db < ND; ++db) o[db] *= alpha;
+    }
+    // A lane whose row has seen no visible key yet keeps m = -inf; its
+    // weights are exp2(-inf) = 0 either way.
+    const float m_use = m == kNegInf ? 0.f : m;
+
+    // P = exp2(c*s - m), rounded to T; l accumulates the rounded weights so
+    // that O's normalisation matches the weights P V actually used.  Masked
+    // scores are -inf and c > 0, so their weight is exp2(-inf) = 0.
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        Frag f;
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+          const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * jj + i], c, -m_use));
+          const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * jj + i + 1], c, -m_use));
+          const Pair pr = H::pack(e0, e1);
+          rs = H::sum2(pr, rs);
+          f[i] = pr[0];
+          f[i + 1] = pr[1];
+        }
+        pf[kb][jj] = f;
+      }
+    l += rs;
+  };
+
+  // K(0) must be resident before slot 0; the Q loads above land with it.
+  wait_loads();
+  barrier();
+
+  // Global slots: in slot 2t group A runs M(t) and group B runs V(t-1); in
+  // slot 2t+1 group A runs V(t) and group B runs M(t).  Both groups execute
+  // the same sequence M(0) V(0) M(1) V(1) ..., group B one slot later (it
+  // idles through slot 0).  Group A loads the tiles: at the start of slot 2t
+  // it issues K(t+1) and V(t), which overwrite K(t-1) and V(t-2) (last read
+  // in slot 2t-1) and are first read in slot 2t+2; it waits for them before
+  // the barrier that closes slot 2t+1.
+  if (group_b) barrier();
+  for (int t = 0; t <= n_tiles; ++t) {
+    if (!group_b) {
+      issue_k(t + 1);
+      issue_v(t);
+    }
+    m_phase(t);
+    barrier();
+    v_phase(t);
+    if (!group_b) wait_loads();
+    barrier();
   }
+  if (!group_b) barrier();
 
   // ---- epilogue: O = O_acc / l, written once; LSE = (m + log2 l) * ln 2 ----
   const float lt = halves_sum(l);
@@ -353,7 +429,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_f16_kernel(KernelParams p) {
 
 template <typename T, int D, bool CAUSAL>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
-  constexpr int NW = 8, BC = 64, BR = NW * 32;
+  constexpr int BR = 256;
   static_assert(BR == kRowsPerWorkgroupF16, "rows per workgroup");
   KernelParams p;
   p.q = a.q;
@@ -363,10 +439,13 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   p.lse = a.lse;
   p.N = a.N;
   p.n_qblk = (int32_t)((a.N + BR - 1) / BR);
-  p.c = __builtin_fabsf(a.scale) * kLog2e;
+  // |scale| * log2(e); a zero scale becomes the smallest normal float so
+  // that masked (-inf) scores still map to -inf and every visible score to
+  // exp2(0) = 1.
+  p.c = __builtin_fmaxf(__builtin_fabsf(a.scale) * kLog2e, 1.17549435e-38f);
   p.q_sign = a.scale < 0.f ? 0x80008000u : 0u;
-  hipLaunchKernelGGL((fwd_f16_kernel<T, D, CAUSAL, NW, BC>), dim3((unsigned)(a.BH * p.n_qblk)),
-                     dim3(NW * 64), 0, stream, p);
+  hipLaunchKernelGGL((fwd_f16_kernel<T, D, CAUSAL>), dim3((unsigned)(a.BH * p.n_qblk)), dim3(512),
+                     0, stream, p);
   return hipGetLastError();
 }
 
