@@ -43,6 +43,8 @@
 //     kRescaleSlack, and in exact arithmetic the result is unchanged because
 //     numerator and denominator share the reference.  This removes the
 //     accumulator rescale from almost every tile.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -154,6 +156,33 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(lds_char*)const_cast<void*>(p);
 }
 
+// Register fences.  The compiler may move plain arithmetic across
+// s_barrier (only memory effects are ordered by it); an empty volatile asm
+// that reads and rewrites a value pins the computation of that value before
+// the fence and every later use after it, which keeps each phase's work
+// inside its slot.
+template <typename V>
+__device__ __forceinline__ void fence(V& x) {
+  asm volatile("" : "+v"(x));
+}
+
+// Maximum of n values get(0..n-1) as a balanced tree of three-input maxima
+// (v_max3_f32), so the dependency chain is log3(n) deep instead of n.
+template <int n, typename Get>
+__device__ __forceinline__ float tree_max(Get get) {
+  if constexpr (n == 1) {
+    return get(0);
+  } else if constexpr (n == 2) {
+    return fmaxf(get(0), get(1));
+  } else {
+    constexpr int a = (n + 2) / 3, b = (n - a + 1) / 2, c = n - a - b;
+    const float x = tree_max<a>(get);
+    const float y = tree_max<b>([&](int i) { return get(a + i); });
+    const float z = tree_max<c>([&](int i) { return get(a + b + i); });
+    return fmaxf(fmaxf(x, y), z);
+  }
+}
+
 template <typename T, int D, bool CAUSAL>
 __global__ void __launch_bounds__(512, 1) fwd_f16_kernel(KernelParams p) {
   using H = Half<T>;
@@ -200,7 +229,7 @@ __global__ void __launch_bounds__(512, 1) fwd_f16_kernel(KernelParams p) {
   const int wave_tiles = qw < N ? (int)((wave_end + BC - 1) / BC) : 0;
 
   // ---- tile loads: global -> LDS, 16 bytes per lane -------------------------
-  // Group A (four waves) loads every tile.  Load j of group-wave gw
+  // Group B (four waves) loads every tile.  Load j of group-wave gw
   // covers rows (gw*LPW + j)*RPL .. +RPL of the tile; lane i fills LDS chunk
   // slot i%CPR of row .. + i/CPR, which holds global chunk slot ^ mask(row).
   int kvoff[LPW], vvoff[LPW];
@@ -252,7 +281,7 @@ __global__ void __launch_bounds__(512, 1) fwd_f16_kernel(KernelParams p) {
       qf[ks] = bits<Frag>(raw);
     }
   }
-  if (!group_b) issue_k(0);
+  if (group_b) issue_k(0);
 
   // ---- lane-constant LDS read offsets ----------------------------------------
   // K A operand for MFMA ks of key block kb: row kb*32 + krow, chunk 2*ks + hh
@@ -285,42 +314,76 @@ __global__ void __launch_bounds__(512, 1) fwd_f16_kernel(KernelParams p) {
   float l = 0.f;      // this lane's share of the row sum (keys it holds)
   const float c = p.c;
 
-  // M phase of tile t: O += P(t-1) V(t-1), then S(t) = K(t) Q^T.
-  auto m_phase = [&](int t) {
-    __builtin_amdgcn_s_setprio(1);
-    if (t >= 1 && t - 1 < wave_tiles) {
-      const char* vl = &smem[1][(t - 1) & 1][0];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-          for (int db = 0; db < ND; ++db) {
-            const int off = (kb * 32 + 16 * jj) * RB + voff[db];
-            const u32x2 lo = lds_read_tr(vl, off);
-            const u32x2 hi = lds_read_tr(vl, off + 4 * RB);
-            const Frag a = bits<Frag>(u32x4{lo[0], lo[1], hi[0], hi[1]});
-            o[db] = H::mma(a, pf[kb][jj], o[db]);
-          }
+  // M phase of tile t: O += P(t-1) V(t-1), then S(t) = K(t) Q^T: NPV + NS
+  // matrix products whose A operands come from LDS.  In the steady state
+  // (m_pv_s) the operand reads run kPipe products ahead of the products, so
+  // LDS latency hides under the matrix pipe; the sched_group_barrier pairs
+  // pin that order.  A wave's first tile has no P V product and its last
+  // (t = wave_tiles) no score product (m_s, m_pv).
+  constexpr int NPV = NKB * 2 * ND;  // O^T += V^T P^T products
+  constexpr int NS = NKS * NKB;      // S^T = K Q^T products
+  constexpr int kPipe = 4;
+  auto fetch = [&](const char* vl, const char* kl, int i) -> Frag {
+    if (i < NPV) {
+      const int kb = i / (2 * ND), jj = (i / ND) % 2, db = i % ND;
+      const int off = (kb * 32 + 16 * jj) * RB + voff[db];
+      const u32x2 lo = lds_read_tr(vl, off);
+      const u32x2 hi = lds_read_tr(vl, off + 4 * RB);
+      return bits<Frag>(u32x4{lo[0], lo[1], hi[0], hi[1]});
     }
-    if (t < wave_tiles) {
-      const char* kl = &smem[0][t & 1][0];
+    const int j = i - NPV, ks = j / NKB, kb = j % NKB;
+    return bits<Frag>(*(const u32x4*)(kl + kb * 32 * RB + koff[ks]));
+  };
+  auto apply = [&](int i, Frag a) {
+    if (i < NPV) {
+      const int kb = i / (2 * ND), jj = (i / ND) % 2, db = i % ND;
+      o[db] = H::mma(a, pf[kb][jj], o[db]);
+    } else {
+      const int j = i - NPV, ks = j / NKB, kb = j % NKB;
+      s[kb] = H::mma(a, qf[ks], s[kb]);
+    }
+  };
+  auto m_pv_s = [&](int t) {
+    const char* vl = &smem[1][(t - 1) & 1][0];
+    const char* kl = &smem[0][t & 1][0];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+    Frag ring[kPipe];
+    constexpr int PRE = 2 * kPipe;  // the first kPipe products are P V products
+    static_assert(kPipe <= NPV, "pipeline prologue");
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
+    for (int i = 0; i < kPipe; ++i) ring[i] = fetch(vl, kl, i);
+    __builtin_amdgcn_sched_group_barrier(0x100, PRE, 0);
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const Frag a = bits<Frag>(*(const u32x4*)(kl + kb * 32 * RB + koff[ks]));
-          s[kb] = H::mma(a, qf[ks], s[kb]);
+    for (int i = 0; i < NPV + NS; ++i) {
+      const Frag a = ring[i % kPipe];
+      if (i + kPipe < NPV + NS) ring[i % kPipe] = fetch(vl, kl, i + kPipe);
+      apply(i, a);
+      if (i + kPipe < NPV + NS) {
+        if (i + kPipe < NPV) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        } else {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
-    __builtin_amdgcn_s_setprio(0);
+  };
+  auto m_pv = [&](int t) {
+    const char* vl = &smem[1][(t - 1) & 1][0];
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) apply(i, fetch(vl, vl, i));
+  };
+  auto m_s = [&](int t) {
+    const char* kl = &smem[0][t & 1][0];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+#pragma unroll
+    for (int i = NPV; i < NPV + NS; ++i) apply(i, fetch(kl, kl, i));
   };
 
   // V phase of tile t: online softmax of S(t) into P(t).
   auto v_phase = [&](int t) {
-    if (t >= wave_tiles) return;
     const int64_t k0 = (int64_t)t * BC;
     // Keys k0 + i with i >= lim are invisible (past N, or after the query
     // when causal): their scores become -inf.  Register r of key block kb
@@ -328,22 +391,16 @@ __global__ void __launch_bounds__(512, 1) fwd_f16_kernel(KernelParams p) {
     int64_t lim64 = N - k0;
     if (CAUSAL && qrow + 1 - k0 < lim64) lim64 = qrow + 1 - k0;
     const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > qw);
-    float mx = kNegInf;
     if (need_mask) {
       const int lim = (int)(lim64 < 0 ? 0 : (lim64 > BC ? BC : lim64)) - 8 * hh;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
+        for (int r = 0; r < 16; ++r)
           if (kb * 32 + key_of_reg(r, 0) >= lim) s[kb][r] = kNegInf;
-          mx = fmaxf(mx, s[kb][r]);
-        }
-    } else {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
     }
+    // Row maximum as a tree (short dependency chains), then across halves.
+    float mx = tree_max<NKB * 16>([&](int i) { return s[i / 16][i % 16]; });
     mx = halves_max(mx);
     const float mxc = mx * c;  // c > 0, so -inf stays -inf
 
@@ -365,24 +422,35 @@ __global__ void __launch_bounds__(512, 1) fwd_f16_kernel(KernelParams p) {
     // P = exp2(c*s - m), rounded to T; l accumulates the rounded weights so
     // that O's normalisation matches the weights P V actually used.  Masked
     // scores are -inf and c > 0, so their weight is exp2(-inf) = 0.
-    float rs = 0.f;
+    // One partial sum per fragment keeps the sum chains short.
+    float rs[NKB * 2];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
-        Frag f;
+        u32x4 f;
+        float acc = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-          const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * jj + i], c, -m_use));
-          const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * jj + i + 1], c, -m_use));
+        for (int i = 0; i < 4; ++i) {
+          const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * jj + 2 * i], c, -m_use));
+          const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * jj + 2 * i + 1], c, -m_use));
           const Pair pr = H::pack(e0, e1);
-          rs = H::sum2(pr, rs);
-          f[i] = pr[0];
-          f[i + 1] = pr[1];
+          acc = H::sum2(pr, acc);
+          f[i] = bits<uint32_t>(pr);
         }
-        pf[kb][jj] = f;
+        rs[kb * 2 + jj] = acc;
+        pf[kb][jj] = bits<Frag>(f);
       }
-    l += rs;
+    float rsum = 0.f;
+#pragma unroll
+    for (int i = 0; i < NKB * 2; ++i) rsum += rs[i];
+    l += rsum;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) fence(pf[kb][jj]);
+    fence(l);
+    fence(m);
   };
 
   // K(0) must be resident before slot 0; the Q loads above land with it.
@@ -391,23 +459,40 @@ __global__ void __launch_bounds__(512, 1) fwd_f16_kernel(KernelParams p) {
 
   // Global slots: in slot 2t group A runs M(t) and group B runs V(t-1); in
   // slot 2t+1 group A runs V(t) and group B runs M(t).  Both groups execute
-  // the same sequence M(0) V(0) M(1) V(1) ..., group B one slot later (it
-  // idles through slot 0).  Group A loads the tiles: at the start of slot 2t
-  // it issues K(t+1) and V(t), which overwrite K(t-1) and V(t-2) (last read
-  // in slot 2t-1) and are first read in slot 2t+2; it waits for them before
-  // the barrier that closes slot 2t+1.
-  if (group_b) barrier();
-  for (int t = 0; t <= n_tiles; ++t) {
-    if (!group_b) {
-      issue_k(t + 1);
-      issue_v(t);
-    }
-    m_phase(t);
+  // the same sequence M(0) V(0) M(1) V(1) ... M(n_tiles) V(n_tiles), group B
+  // one slot later (it idles through slot 0).  Group B loads the tiles, at the
+  // start of its V phases: at the start of slot 2t+2 it issues K(t+2) and
+  // V(t+1), which overwrite K(t) and V(t-1) (last read in slot 2t+1) and are
+  // first read in slot 2t+4; it waits for them at the end of its next M phase
+  // (slot 2t+3), before the barrier that closes that slot.  A wave works on
+  // tiles t < wave_tiles only (causal waves above the diagonal stop early)
+  // but takes part in every slot's barrier.
+  auto iteration = [&](int t, auto mwork, auto vwork) {
+    mwork();
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) fence(s[kb]);
+#pragma unroll
+    for (int db = 0; db < ND; ++db) fence(o[db]);
+    if (group_b) wait_loads();
     barrier();
-    v_phase(t);
-    if (!group_b) wait_loads();
+    if (group_b) {
+      issue_k(t + 2);
+      issue_v(t + 1);
+    }
+    vwork();
+    barrier();
+  };
+  const int W = wave_tiles;
+  if (group_b) {
+    issue_k(1);
+    issue_v(0);
     barrier();
   }
+  iteration(
+      0, [&] { if (W >= 1) m_s(0); }, [&] { if (W >= 1) v_phase(0); });
+  for (int t = 1; t < W; ++t) iteration(t, [&] { m_pv_s(t); }, [&] { v_phase(t); });
+  if (W >= 1) iteration(W, [&] { m_pv(W); }, [] {});
+  for (int t = W >= 1 ? W + 1 : 1; t <= n_tiles; ++t) iteration(t, [] {}, [] {});
   if (!group_b) barrier();
 
   // ---- epilogue: O = O_acc / l, written once; LSE = (m + log2 l) * ln 2 ----
