@@ -48,7 +48,7 @@ def build_library(verbose: bool = False, extra_flags=()) -> str:
     objs = []
     for src in KERNEL_SOURCES:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-        _run([cc, f"--offload-arch={ARCH}", *common,
+        _run([cc, f"--offload-arch={ARCH}", *common, "-fno-honor-nans",
               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
               "-c", os.path.join(CSRC, src), "-o", obj], verbose)
         objs.append(obj)
