@@ -7,11 +7,28 @@ the causal mask), the roofline of the kernel against the MI355X dense MFMA
 peak, and the fp64 CPU oracle timed on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Counter workflow (HBM traffic per launch, rocprofv3 on the GPU host):
+
+    rocprofv3 --pmc FETCH_SIZE -f csv -d OUT/fetch -o fetch -- \\
+        python3 bench.py --steps 5 --warmup 1 --cpu-budget 0 --copy-calibration
+    rocprofv3 --pmc WRITE_SIZE -f csv -d OUT/write -o write -- \\
+        python3 bench.py --steps 5 --warmup 1 --cpu-budget 0 --copy-calibration
+    python3 bench.py --summarize-traffic OUT/fetch/fetch_counter_collection.csv \\
+        OUT/write/write_counter_collection.csv
+
+--copy-calibration adds device-to-device copies of a known size after the
+timed region; the counters of those copies turn FETCH_SIZE / WRITE_SIZE into
+bytes (the factor is reported).  --summarize-traffic writes
+profiles/traffic_<workload>.md, which later runs read back for the roofline's
+"traffic" figure while the kernel source is unchanged.
 """
 import argparse
+import csv
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -22,26 +39,38 @@ if ROOT not in sys.path:
 # MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s).
 MFMA_PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3}
 HBM_PEAK_GBPS = 8000.0
-KERNEL_SOURCE = os.path.join(ROOT, "io_aware_tiled_08_amd", "csrc", "fa_fwd_f16.hip")
+KERNEL_SOURCES = {
+    "f16": os.path.join(ROOT, "io_aware_tiled_08_amd", "csrc", "fa_fwd_f16.hip"),
+    "bf16": os.path.join(ROOT, "io_aware_tiled_08_amd", "csrc", "fa_fwd_f16.hip"),
+    "f32": os.path.join(ROOT, "io_aware_tiled_08_amd", "csrc", "fa_fwd_f32.hip"),
+}
+KERNEL_NAME_PATTERN = {"f16": "fwd_f16_kernel", "bf16": "fwd_f16_kernel", "f32": "fwd_f32_kernel"}
 PROFILES = os.path.join(ROOT, "profiles")
+COPY_BYTES = 512 << 20  # one calibration copy: 512 MiB read + 512 MiB written
+COPY_REPS = 3
 
 
-def kernel_source_digest() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
+def kernel_source_digest(dtype: str) -> str:
+    with open(KERNEL_SOURCES[dtype], "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when there is none or the kernel source changed since it was taken."""
-    path = os.path.join(PROFILES, f"traffic_{workload}.json")
+def traffic_path(workload: str) -> str:
+    return os.path.join(PROFILES, f"traffic_{workload}.md")
+
+
+def measured_traffic(workload: str, dtype: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the kernel source changed since it was taken."""
+    path = traffic_path(workload)
     if not os.path.exists(path):
         return None
-    with open(path) as f:
-        t = json.load(f)
-    if t.get("kernel_source_sha256") != kernel_source_digest():
+    text = open(path).read()
+    sha = re.search(r"^kernel_source_sha256:\s*([0-9a-f]{64})\s*$", text, re.M)
+    val = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)\s*$", text, re.M)
+    if not sha or not val or sha.group(1) != kernel_source_digest(dtype):
         return None
-    return t.get("hbm_bytes_per_launch")
+    return float(val.group(1))
 
 
 def cpu_baseline(w, q, k, v, budget_s: float):
@@ -76,6 +105,80 @@ def cpu_baseline(w, q, k, v, budget_s: float):
     }
 
 
+def _counter_rows(path, counter):
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+def summarize_traffic(fetch_csv: str, write_csv: str, workload: str) -> str:
+    """Turns two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per
+    dispatch) of `bench.py --copy-calibration` into HBM bytes per launch of
+    the attention kernel, scaled by what the same counters read for the
+    calibration copies, and writes profiles/traffic_<workload>.md."""
+    from io_aware_tiled_08_amd import workloads as W
+    w = W.WORKLOADS[workload]
+    pat = KERNEL_NAME_PATTERN[w.dtype]
+    out = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _counter_rows(path, counter)
+        fa = [v for n, v in rows if pat in n]
+        cp = [v for n, v in rows if "copy" in n.lower() or "elementwise" in n.lower()]
+        cp = [v for v in cp if v > 0.5 * COPY_BYTES / 1024]  # the 512 MiB copies only
+        if not fa or not cp:
+            raise SystemExit(f"{path}: no {counter} rows for the kernel ({len(fa)}) or the copy ({len(cp)})")
+        copy_kib = sum(cp) / len(cp)
+        factor = (COPY_BYTES / 1024) / copy_kib
+        fa_kib = sum(fa) / len(fa)
+        out[counter] = {"kernel_kib": fa_kib, "copy_kib": copy_kib, "factor": factor,
+                        "bytes": fa_kib * 1024 * factor, "n": len(fa)}
+    total = out["FETCH_SIZE"]["bytes"] + out["WRITE_SIZE"]["bytes"]
+    comp = w.compulsory_bytes()
+    os.makedirs(PROFILES, exist_ok=True)
+    lines = [
+        f"# HBM traffic of the forward kernel, workload {workload}",
+        "",
+        f"Workload: {w.description}.  Compulsory bytes (Q, K, V read once; O and fp32 LSE",
+        f"written once): {comp} ({comp / 2**20:.2f} MiB).",
+        "",
+        "Commands (GPU host, from the repository root):",
+        "",
+        "    rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/traffic_" + workload + "/fetch -o fetch -- \\",
+        f"        python3 bench.py --workload {workload} --steps 5 --warmup 1 --cpu-budget 0 --copy-calibration",
+        "    rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/traffic_" + workload + "/write -o write -- \\",
+        f"        python3 bench.py --workload {workload} --steps 5 --warmup 1 --cpu-budget 0 --copy-calibration",
+        "    python3 bench.py --workload " + workload + " --summarize-traffic \\",
+        "        gpurun_out/traffic_" + workload + "/fetch/fetch_counter_collection.csv \\",
+        "        gpurun_out/traffic_" + workload + "/write/write_counter_collection.csv",
+        "",
+        "| counter | kernel KiB/dispatch (mean) | dispatches | 512 MiB copy reads as KiB | scale factor | bytes/launch |",
+        "|---|---|---|---|---|---|",
+    ]
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        o = out[counter]
+        lines.append(f"| {counter} | {o['kernel_kib']:.1f} | {o['n']} | {o['copy_kib']:.1f} | "
+                     f"{o['factor']:.4f} | {o['bytes']:.0f} |")
+    lines += [
+        "",
+        f"HBM bytes per launch (fetch + write, calibrated): {total:.0f} "
+        f"({total / comp:.3f} x compulsory).",
+        "",
+        "Machine-readable (bench.py reads these; traffic is reported only while the",
+        "kernel source hash matches):",
+        "",
+        f"hbm_bytes_per_launch: {total:.0f}",
+        f"kernel_source_sha256: {kernel_source_digest(w.dtype)}",
+        "",
+    ]
+    path = traffic_path(workload)
+    with open(path, "w") as f:
+        f.write("\n".join(lines))
+    return path
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -84,7 +187,18 @@ def main():
     ap.add_argument("--workload", default=None)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle time for cpu_baseline (0 = skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed region, run device copies of a known size "
+                         "(for calibrating rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_<workload>.md from two rocprofv3 --pmc runs")
     args = ap.parse_args()
+
+    from io_aware_tiled_08_amd import workloads as W
+    name = args.workload or W.HEADLINE
+    if args.summarize_traffic:
+        print(summarize_traffic(*args.summarize_traffic, name))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the forward pass "
               "shards by (batch, head) with no communication, and this build measures "
@@ -94,12 +208,10 @@ def main():
     import torch
 
     from io_aware_tiled_08_amd import binding, flash_attn_fwd
-    from io_aware_tiled_08_amd import workloads as W
     if not os.path.exists(binding.library_path()):
         from io_aware_tiled_08_amd.build import build_library
         build_library()
 
-    name = args.workload or W.HEADLINE
     w = W.WORKLOADS[name]
     q, k, v = W.workload_inputs(w)
     dev = torch.device("cuda:0")
@@ -114,6 +226,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    # HIP events recorded on the stream the kernel is launched on.
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -123,12 +236,20 @@ def main():
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = start.elapsed_time(end) / args.steps
+    ms = start.elapsed_time(end) / args.steps  # one launch per step
+
+    if args.copy_calibration:
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(COPY_REPS):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     flops = w.flops()
     tflops = flops / (ms * 1e-3) / 1e12
     peak = MFMA_PEAK_TFLOPS[w.dtype]
-    traffic = measured_traffic(name)
+    traffic = measured_traffic(name, w.dtype)
     roofline = {
         "bound": "mfma",
         "achieved": round(tflops, 2),
@@ -136,8 +257,10 @@ def main():
         "unit": "TFLOP/s",
         "frac": round(tflops / peak, 4),
         "traffic": traffic,
+        "kernel_ms": round(ms, 5),
         "compulsory_bytes": w.compulsory_bytes(),
         "compulsory_GBps": round(w.compulsory_bytes() / (ms * 1e-3) / 1e9, 1),
+        "compulsory_frac_of_hbm_peak": round(w.compulsory_bytes() / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
     }
     props = torch.cuda.get_device_properties(dev)
     result = {
