@@ -16,24 +16,26 @@
 //
 // CDNA4 mapping (our design, not the pages'):
 //   * Workgroup = 8 waves x 32 query rows, in two groups of four (waves 0-3
-//     and 4-7; wave w runs on SIMD w % 4, so every SIMD holds one wave of each
-//     group).  The groups run half a tile apart ("ping-pong"): while one group
-//     issues matrix products (M phase) the other runs the softmax on the
-//     vector ALU (V phase), and a workgroup barrier swaps the roles.  For the
-//     tile t a wave's M phase is  O += P(t-1) V(t-1)  followed by  S(t) =
-//     K(t) Q^T, and its V phase turns S(t) into P(t).  The M-phase wave runs
-//     at raised priority so its matrix instructions issue first.
-//   * K and V tiles (64 keys) are double buffered in LDS and filled by
-//     buffer_load ... lds (HBM/L2 straight into LDS, no register staging).
-//     Each row's 16-byte chunks are stored XOR-permuted so that the operand
-//     reads hit all LDS banks; the permutation is applied on the global side
-//     (lane i of a load always writes LDS bytes 16i..16i+15).  Loads for tile
-//     t+1 are issued one tile ahead and only waited for at the barrier before
-//     their first use.
+//     and 4-7; wave w and wave w+4 share a SIMD).  The groups run half a tile
+//     apart ("ping-pong"): while one group issues the matrix products of its
+//     tile (M phase) the other runs its softmax on the vector ALU (V phase),
+//     and a workgroup barrier swaps the roles.  For tile t a wave's M phase is
+//     O += P(t-1) V(t-1) followed by S(t) = K(t) Q^T, and its V phase turns
+//     S(t) into P(t).  (On gfx950 a 32x32x16 MFMA blocks its SIMD's vector
+//     issue for most of its 32 cycles, so ordinary vector work barely hides
+//     under matrix work; the alternation gives each phase whole slots.)
+//   * K and V tiles (128 keys) are double buffered in LDS and filled by
+//     buffer_load ... lds (HBM/L2 straight into LDS, no register staging),
+//     issued by the group entering its V phase.  Each row's 16-byte chunks
+//     are stored XOR-permuted so that the operand reads hit all LDS banks;
+//     the permutation is applied on the global side (lane i of a load always
+//     writes LDS bytes 16i..16i+15).  Loads for a tile are issued one tile
+//     ahead and only waited for at the barrier before their first use.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_{f16,bf16}: a lane owns one query
-//     (accumulator column) and 16 keys, the other 16 sit in lane l^32, so the
-//     row max and sum are in-lane plus one v_permlane32_swap, and the rescale
-//     factor is a per-lane scalar.  Q stays in registers for the whole loop.
+//     (accumulator column) and 16 keys of each 32-key block, the other 16 sit
+//     in lane l^32, so the row max and sum are in-lane plus one
+//     v_permlane32_swap, and the rescale factor is a per-lane scalar.  Q stays
+//     in registers for the whole loop.
 //   * O^T += V^T P^T: P^T is the B operand taken straight from the score
 //     registers (rounded to the input type), V^T comes from row-major V in
 //     LDS through ds_read_b64_tr_b16 transposing loads.
@@ -191,7 +193,7 @@ __global__ void __launch_bounds__(512, 1) fwd_f16_kernel(KernelParams p) {
   using Sw = Swizzle<D>;
   constexpr int NW = 8;              // waves per workgroup
   constexpr int BR = NW * 32;        // query rows per workgroup
-  constexpr int BC = 64;             // keys per tile
+  constexpr int BC = 128;            // keys per tile
   constexpr int RB = D * 2;          // bytes per row of K or V
   constexpr int CPR = D / 8;         // 16-byte chunks per row
   constexpr int TILE = BC * RB;      // bytes of one staged K (or V) tile
