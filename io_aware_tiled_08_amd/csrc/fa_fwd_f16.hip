@@ -45,8 +45,6 @@
 //     kRescaleSlack, and in exact arithmetic the result is unchanged because
 //     numerator and denominator share the reference.  This removes the
 //     accumulator rescale from almost every tile.
-#include <type_traits>
-
 #include "fa_device.h"
 #include "fa_launch.h"
 
