@@ -199,7 +199,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default: as many as fill 1.5 s, at least 10, so the "
+                         "GPU clocks reach their loaded steady state)")
     ap.add_argument("--workload", default=None)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle time for cpu_baseline (0 = skip)")
@@ -239,8 +241,18 @@ def main():
     def step():
         flash_attn_fwd(qd, kd, vd, o, lse, scale=w.scale, causal=w.causal, stream=stream)
 
-    for _ in range(args.warmup):
-        step()
+    if args.warmup is None:
+        warmup = 0
+        t_w = time.perf_counter()
+        while warmup < 10 or time.perf_counter() - t_w < 1.5:
+            for _ in range(10):
+                step()
+            warmup += 10
+            torch.cuda.synchronize()
+    else:
+        warmup = args.warmup
+        for _ in range(warmup):
+            step()
     torch.cuda.synchronize()
     # HIP events recorded on the stream the kernel is launched on.
     start = torch.cuda.Event(enable_timing=True)
@@ -285,7 +297,7 @@ def main():
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
