@@ -39,6 +39,7 @@ if ROOT not in sys.path:
 # MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s).
 MFMA_PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3}
 HBM_PEAK_GBPS = 8000.0
+PEAK_CLOCK_MHZ = 2400.0  # the engine clock the published MFMA peaks are quoted at
 KERNEL_SOURCES = {
     "f16": os.path.join(ROOT, "io_aware_tiled_08_amd", "csrc", "fa_fwd_f16.hip"),
     "bf16": os.path.join(ROOT, "io_aware_tiled_08_amd", "csrc", "fa_fwd_f16.hip"),
@@ -195,6 +196,83 @@ def summarize_traffic(fetch_csv: str, write_csv: str, workload: str) -> str:
     return path
 
 
+def percentile(sorted_vals, f):
+    """Nearest-rank percentile of an ascending list."""
+    i = min(len(sorted_vals) - 1, max(0, int(round(f * (len(sorted_vals) - 1)))))
+    return sorted_vals[i]
+
+
+class ClockSampler:
+    """Samples the GPU's graphics clock (MHz) through amdsmi in a background
+    thread.  Reading the clock changes no setting; when amdsmi is missing or
+    refuses, no samples are taken and the clock fields are left out."""
+
+    def __init__(self, period_s=0.02):
+        self.period_s = period_s
+        self.samples = []
+        self._stop = None
+        self._thread = None
+
+    def _read(self, amdsmi, h):
+        try:
+            m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+            vals = m.get("current_gfxclks")
+            if isinstance(vals, (list, tuple)):
+                vals = [x for x in vals if isinstance(x, (int, float)) and 0 < x < 10000]
+                if vals:
+                    return sum(vals) / len(vals)
+            x = m.get("current_gfxclk")
+            if isinstance(x, (int, float)) and 0 < x < 10000:
+                return float(x)
+        except Exception:
+            pass
+        info = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
+        x = info.get("clk")
+        return float(x) if isinstance(x, (int, float)) and 0 < x < 10000 else None
+
+    def start(self):
+        import threading
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            handles = amdsmi.amdsmi_get_processor_handles()
+            if not handles:
+                return
+            h = handles[0]
+        except Exception:
+            return
+        self._stop = threading.Event()
+
+        def run():
+            while not self._stop.is_set():
+                try:
+                    x = self._read(amdsmi, h)
+                except Exception:
+                    return
+                if x:
+                    self.samples.append(x)
+                self._stop.wait(self.period_s)
+
+        self._thread = threading.Thread(target=run, daemon=True)
+        self._thread.start()
+
+    def stop(self):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join(timeout=2.0)
+        try:
+            import amdsmi
+            amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
+
+    def median_mhz(self):
+        if not self.samples:
+            return None
+        v = sorted(self.samples)
+        return v[len(v) // 2]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -266,6 +344,22 @@ def main():
     wall = time.perf_counter() - t0
     ms = start.elapsed_time(end) / args.steps  # one launch per step
 
+    # Per-launch distribution: one event pair around each launch, after the
+    # timed region (so the extra event records do not perturb it), with the
+    # graphics clock sampled meanwhile.
+    n_dist = min(args.steps, max(20, int(2.0 / max(ms * 1e-3, 1e-6))))
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(n_dist)]
+    clock = ClockSampler()
+    clock.start()
+    for a, b in pairs:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    clock.stop()
+    per_launch = sorted(a.elapsed_time(b) for a, b in pairs)
+
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
@@ -289,7 +383,15 @@ def main():
         "compulsory_bytes": w.compulsory_bytes(),
         "compulsory_GBps": round(w.compulsory_bytes() / (ms * 1e-3) / 1e9, 1),
         "compulsory_frac_of_hbm_peak": round(w.compulsory_bytes() / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "launch_ms_p10_p50_p90": [round(percentile(per_launch, f), 5) for f in (0.1, 0.5, 0.9)],
+        "launches_sampled": len(per_launch),
     }
+    mhz = clock.median_mhz()
+    if mhz:
+        # The same kernel against the peak at the clock the card actually ran.
+        peak_at_clock = peak * mhz / PEAK_CLOCK_MHZ
+        roofline["gfx_clock_mhz_median"] = round(mhz, 1)
+        roofline["frac_at_measured_clock"] = round(tflops / peak_at_clock, 4)
     props = torch.cuda.get_device_properties(dev)
     result = {
         "metric": "attention fwd TFLOP/s and % of MFMA peak, N=4096 d=128 fp16 (1 GPU)",

@@ -26,7 +26,7 @@ struct FwdArgs {
 
 // Query rows owned by one workgroup (fixes the grid size).
 constexpr int kRowsPerWorkgroupF16 = 256;
-constexpr int kRowsPerWorkgroupF32 = 64;
+constexpr int kRowsPerWorkgroupF32 = 32;
 
 inline int rows_per_workgroup(Dtype dtype) {
   return dtype == Dtype::F32 ? kRowsPerWorkgroupF32 : kRowsPerWorkgroupF16;
