@@ -26,6 +26,15 @@ What it computes (sources: the explainer pages on FlashAttention):
   ``rescale=False`` it is that episode's failing streamer, which updates m but
   never rescales; it exists only so the tests can show that a mistake of that
   kind is caught.
+* ``attention_partial`` is the same definition restricted to a range of keys;
+  a row that sees no key of the range gets LSE = -inf and O = 0.  It is the
+  building block of ``split_attention``.
+* ``merge_partials`` combines results computed over disjoint key ranges with
+  the rescaling rule of EP 04 applied once per range instead of once per tile:
+  with M the largest of the ranges' LSE values, each range's normalised output
+  is weighted by exp(LSE_s - M), the weights are summed, and LSE = M + ln of
+  that sum.  ``split_attention`` = ``attention_partial`` over each range, then
+  ``merge_partials``.
 
 Readings where the pages are silent (each is restated in the test that pins
 it):
@@ -35,6 +44,11 @@ it):
   as a float32, so the oracle uses float64(float32(scale)) as well;
 * causal means query i sees key j iff j <= i (square, diagonal included); the
   pages never treat masking;
+* K and V may be longer than Q (Nk >= Nq rows): the key/value cache of the
+  "KV Cache: Why Generation Speeds Up" card (past keys and values are kept;
+  each new token computes only its own).  The Nq queries are then the last Nq
+  positions of the sequence, so a causal query i sees key j iff
+  j <= i + (Nk - Nq); with Nq = Nk this is the square rule above;
 * LSE is the natural-log log-sum-exp of the scaled, masked scores of a row;
 * inputs are upcast exactly to float64 (fp16, bf16 and fp32 all embed in it).
 
@@ -80,51 +94,121 @@ def _row_index(rows, B: int, H: int, N: int) -> np.ndarray:
     return rows
 
 
-def attention_forward(q, k, v, scale: float, causal: bool = False,
+def _shapes(Q, K, V):
+    if Q.ndim != 4 or K.ndim != 4 or V.shape != K.shape or K.shape[:2] != Q.shape[:2] \
+            or K.shape[3] != Q.shape[3]:
+        raise ValueError("q must be [B, H, Nq, d] and k, v one [B, H, Nk, d] shape")
+    B, H, Nq, d = Q.shape
+    return B, H, Nq, K.shape[2], d
+
+
+def causal_offset(Nq: int, Nk: int) -> int:
+    """Position of query 0 in the key sequence: the queries are its last Nq
+    positions (key/value cache reading).  Causal query i sees keys
+    j <= i + causal_offset(Nq, Nk)."""
+    if Nk < Nq:
+        raise ValueError("causal attention needs at least as many keys as queries")
+    return Nk - Nq
+
+
+def attention_partial(q, k, v, scale: float, causal: bool = False,
+                      k_begin: int = 0, k_end: Optional[int] = None,
                       rows=None, row_block: int = 128
                       ) -> Tuple[np.ndarray, np.ndarray]:
-    """Exact attention forward in float64.
+    """Exact attention of each query row over the keys k_begin <= j < k_end,
+    in float64.
 
-    Returns ``(O, LSE)``: O is [B, H, R, d] and LSE is [B, H, R], where R = N
+    Returns ``(O, LSE)``: O is [B, H, R, d] and LSE is [B, H, R], where R = Nq
     when ``rows`` is None, else the number of requested query rows (``rows`` is
-    [R], shared by all heads, or [B, H, R]).
+    [R], shared by all heads, or [B, H, R]).  A row that sees none of the keys
+    gets O = 0 and LSE = -inf.
 
     Steps per (b, h) and per block of query rows, following the standard
     attention pipeline of the chapter's "Standard vs Flash Attention" section:
-      1. S = scale * Q K^T, every score of the block materialised;
-      2. causal: S[i, j] = -inf for j > i;
+      1. S = scale * Q K^T over the key range, every score materialised;
+      2. causal: S[i, j] = -inf for j > i + (Nk - Nq);
       3. pass 1: m = max_j S[i, j] and l = sum_j exp(S[i, j] - m);
       4. pass 2: P = exp(S - m) / l;
       5. O = P V;  LSE = m + ln l.
     """
     Q, K, V = as_f64(q), as_f64(k), as_f64(v)
-    if Q.ndim != 4 or K.shape != Q.shape or V.shape != Q.shape:
-        raise ValueError("q, k, v must share one [B, H, N, d] shape")
-    B, H, N, d = Q.shape
+    B, H, Nq, Nk, d = _shapes(Q, K, V)
+    off = causal_offset(Nq, Nk) if causal else 0
+    lo = max(0, int(k_begin))
+    hi = Nk if k_end is None else min(Nk, int(k_end))
     s64 = boundary_scale(scale)
-    idx_all = _row_index(rows, B, H, N)
+    idx_all = _row_index(rows, B, H, Nq)
     R = idx_all.shape[-1]
     O = np.zeros((B, H, R, d), dtype=np.float64)
-    LSE = np.zeros((B, H, R), dtype=np.float64)
-    if R == 0 or N == 0:
+    LSE = np.full((B, H, R), -np.inf, dtype=np.float64)
+    if R == 0:
         return O, LSE
     for b in range(B):
         for h in range(H):
             for r0 in range(0, R, row_block):
                 idx = np.asarray(idx_all[b, h, r0:r0 + row_block])
-                # A causal row i sees keys 0..i only, so the block never needs
-                # keys past its largest row.
-                nk = int(idx.max()) + 1 if causal else N
-                S = (Q[b, h, idx] @ K[b, h, :nk].T) * s64
+                # A causal row i sees keys up to i + off only, so the block
+                # never needs keys past its largest row's last one.
+                top = min(hi, int(idx.max()) + 1 + off) if causal else hi
+                if top <= lo:
+                    continue
+                S = (Q[b, h, idx] @ K[b, h, lo:top].T) * s64
                 if causal:
-                    S[np.arange(nk)[None, :] > idx[:, None]] = -np.inf
+                    S[np.arange(lo, top)[None, :] > idx[:, None] + off] = -np.inf
                 m = S.max(axis=1, keepdims=True)
-                E = np.exp(S - m)
+                seen = np.isfinite(m)
+                E = np.exp(S - np.where(seen, m, 0.0))
                 l = E.sum(axis=1, keepdims=True)
-                P = E / l
-                O[b, h, r0:r0 + len(idx)] = P @ V[b, h, :nk]
-                LSE[b, h, r0:r0 + len(idx)] = m[:, 0] + np.log(l[:, 0])
+                P = E / np.where(seen, l, 1.0)
+                O[b, h, r0:r0 + len(idx)] = P @ V[b, h, lo:top]
+                with np.errstate(divide="ignore"):
+                    LSE[b, h, r0:r0 + len(idx)] = np.where(
+                        seen[:, 0], m[:, 0] + np.log(l[:, 0]), -np.inf)
     return O, LSE
+
+
+def attention_forward(q, k, v, scale: float, causal: bool = False,
+                      rows=None, row_block: int = 128
+                      ) -> Tuple[np.ndarray, np.ndarray]:
+    """Exact attention forward in float64: ``attention_partial`` over every
+    key.  Every query row must see at least one key."""
+    O, LSE = attention_partial(q, k, v, scale, causal, 0, None, rows, row_block)
+    if LSE.size and not np.all(np.isfinite(LSE)):
+        raise ValueError("a query row sees no key (Nk = 0?)")
+    return O, LSE
+
+
+def merge_partials(parts) -> Tuple[np.ndarray, np.ndarray]:
+    """Combine (O_s, LSE_s) computed over disjoint key ranges.
+
+    The rescaling rule of the online softmax, once per range: M = max_s LSE_s,
+    w_s = exp(LSE_s - M) (0 for a range the row never saw), O = sum_s w_s O_s /
+    sum_s w_s, LSE = M + ln sum_s w_s.  Every row must have seen some range.
+    """
+    parts = list(parts)
+    if not parts:
+        raise ValueError("nothing to merge")
+    Ls = np.stack([np.asarray(p[1], dtype=np.float64) for p in parts])
+    Os = np.stack([np.asarray(p[0], dtype=np.float64) for p in parts])
+    M = Ls.max(axis=0)
+    if Ls[0].size and not np.all(np.isfinite(M)):
+        raise ValueError("a query row saw no key in any part")
+    w = np.exp(Ls - M)
+    wsum = w.sum(axis=0)
+    O = (w[..., None] * Os).sum(axis=0) / wsum[..., None]
+    return O, M + np.log(wsum)
+
+
+def split_attention(q, k, v, scale: float, causal: bool = False, bounds=None,
+                    rows=None) -> Tuple[np.ndarray, np.ndarray]:
+    """Attention over the key ranges [bounds[s], bounds[s+1]) separately, then
+    merged: the split-key form of the same result."""
+    Nk = as_f64(k).shape[2]
+    b = [0, Nk] if bounds is None else [int(x) for x in bounds]
+    if b[0] != 0 or b[-1] != Nk or any(x > y for x, y in zip(b, b[1:])):
+        raise ValueError("bounds must rise from 0 to Nk")
+    return merge_partials(attention_partial(q, k, v, scale, causal, lo, hi, rows)
+                          for lo, hi in zip(b, b[1:]))
 
 
 def streaming_attention(q, k, v, scale: float, causal: bool = False,
@@ -138,14 +222,16 @@ def streaming_attention(q, k, v, scale: float, causal: bool = False,
     take the tile's scores and their maximum t; if t > m, scale l and acc by
     exp(m - t) (skipped when ``rescale`` is False) and set m = t; then add
     exp(s_j - m) to l and exp(s_j - m) * v_j to acc.  Finally O = acc / l and
-    LSE = m + ln l.  Keys a causal row may not see are left out of its tiles.
+    LSE = m + ln l.  Keys a causal row may not see (j > i + Nk - Nq) are left
+    out of its tiles.
     """
     if tile < 1:
         raise ValueError("tile must be >= 1")
     Q, K, V = as_f64(q), as_f64(k), as_f64(v)
-    B, H, N, d = Q.shape
+    B, H, Nq, Nk, d = _shapes(Q, K, V)
+    off = causal_offset(Nq, Nk) if causal else 0
     s64 = boundary_scale(scale)
-    idx_all = _row_index(rows, B, H, N)
+    idx_all = _row_index(rows, B, H, Nq)
     R = idx_all.shape[-1]
     O = np.zeros((B, H, R, d), dtype=np.float64)
     LSE = np.zeros((B, H, R), dtype=np.float64)
@@ -153,7 +239,7 @@ def streaming_attention(q, k, v, scale: float, causal: bool = False,
         for h in range(H):
             for r, i in enumerate(idx_all[b, h]):
                 i = int(i)
-                n_visible = i + 1 if causal else N
+                n_visible = i + 1 + off if causal else Nk
                 m = -math.inf
                 l = 0.0
                 acc = np.zeros(d, dtype=np.float64)
