@@ -15,7 +15,7 @@
  * Conventions shared by every entry point
  *   - All functions are extern "C", never throw, and report errors through
  *     fa_status.  No entry point allocates device memory or keeps a pointer
- *     after it returns.
+ *     after it returns; scratch memory, where a path needs it, is passed in.
  *   - Argument checks run before any HIP runtime call, so a host without a
  *     GPU can exercise every error path.
  */
@@ -28,7 +28,7 @@
 extern "C" {
 #endif
 
-#define FA_MI355X_ABI_VERSION 1
+#define FA_MI355X_ABI_VERSION 2
 
 typedef enum {
   FA_F32 = 0,   /* IEEE binary32 */
@@ -47,7 +47,8 @@ typedef enum {
   FA_ERR_ALIAS = 7,      /* o or lse overlaps an input or each other */
   FA_ERR_NO_DEVICE = 8,  /* no HIP device is usable */
   FA_ERR_ARCH = 9,       /* the current device is not gfx950 */
-  FA_ERR_HIP = 10        /* the HIP runtime reported an error (see last_error) */
+  FA_ERR_HIP = 10,       /* the HIP runtime reported an error (see last_error) */
+  FA_ERR_WORKSPACE = 11  /* a needed workspace is NULL or smaller than required */
 } fa_status;
 
 /*
@@ -100,6 +101,70 @@ fa_status flash_attn_fwd(const void* q, const void* k, const void* v,
                          int64_t B, int64_t H, int64_t N, int64_t d,
                          float scale, int causal,
                          fa_dtype dtype, void* stream);
+
+/*
+ * flash_attn_fwd_kvcache -- attention of Nq new queries against a key/value
+ * cache of Nk rows (decode), fp16 or bf16.
+ *
+ * Source: "KV Cache: Why Generation Speeds Up" (generation stores and reuses
+ * the keys and values of earlier tokens) for the operation; the computation is
+ * the one of flash_attn_fwd (same pages).  Reading where the pages are silent:
+ * the Nq queries are the last Nq positions of the sequence whose Nk keys are
+ * cached, so with causal != 0 query i sees the keys j <= i + (Nk - Nq); with
+ * Nq == Nk that is flash_attn_fwd's mask.
+ *
+ * For each b < B, h < H and query row i < Nq:
+ *   s_ij   = scale * sum_c q[b,h,i,c] * k[b,h,j,c]      for visible keys j < Nk
+ *   o[b,h,i,:] = sum_j softmax_j(s_ij) * v[b,h,j,:]
+ *   lse[b,h,i] = ln(sum_j exp(s_ij))
+ *
+ * Arguments
+ *   q        device pointer, read only, contiguous [B, H, Nq, d] of `dtype`.
+ *   k, v     device pointers, read only, contiguous [B, H, Nk, d] of `dtype`.
+ *   o        device pointer, contiguous [B, H, Nq, d] of `dtype`; overwritten.
+ *   lse      device pointer, contiguous [B, H, Nq] float32; overwritten.
+ *   B, H, Nq, Nk  each >= 0; nothing is done when B, H or Nq is 0.  Nk must be
+ *            >= 1, and >= Nq when causal.
+ *   d        64 or 128.
+ *   scale, causal  as for flash_attn_fwd.
+ *   num_splits  number of key ranges computed by separate workgroups and then
+ *            merged (each range's normalised output weighted by exp(its LSE -
+ *            the largest LSE), the online-softmax rescale rule); <= 0 lets the
+ *            library choose.  The count actually used is
+ *            flash_attn_kvcache_splits(B, H, Nq, Nk, d, num_splits).
+ *   workspace, workspace_bytes  device scratch owned by the caller, 16-byte
+ *            aligned, at least flash_attn_kvcache_workspace_size(B, H, Nq, Nk,
+ *            d, num_splits) bytes (0 when one split is used: then workspace
+ *            may be NULL).  Its contents on entry do not matter; on return it
+ *            holds partial results the caller may discard.  Calls that share
+ *            a workspace must be ordered on one stream.
+ *   dtype    FA_F16 or FA_BF16 (FA_F32 returns FA_ERR_DTYPE).
+ *   stream   as for flash_attn_fwd.
+ *
+ * Enqueues one kernel (one split) or two (the ranges, then their merge) and
+ * returns without synchronising.  o, lse and the workspace must not overlap
+ * each other or q, k, v (FA_ERR_ALIAS).  Errors as for flash_attn_fwd, plus
+ * FA_ERR_WORKSPACE when the workspace is NULL or too small.
+ */
+fa_status flash_attn_fwd_kvcache(const void* q, const void* k, const void* v,
+                                 void* o, float* lse,
+                                 int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                                 int64_t d, float scale, int causal,
+                                 int num_splits, void* workspace,
+                                 int64_t workspace_bytes,
+                                 fa_dtype dtype, void* stream);
+
+/* Key ranges flash_attn_fwd_kvcache uses for these sizes and num_splits (1
+ * for empty or invalid sizes).  No HIP call. */
+int flash_attn_kvcache_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                              int64_t d, int num_splits);
+
+/* Workspace bytes flash_attn_fwd_kvcache needs for these sizes and
+ * num_splits: splits * B * H * Nq * (d + 1) * 4 when more than one split is
+ * used, else 0; -1 if that size overflows.  No HIP call. */
+int64_t flash_attn_kvcache_workspace_size(int64_t B, int64_t H, int64_t Nq,
+                                          int64_t Nk, int64_t d,
+                                          int num_splits);
 
 /* Static, never-NULL description of a status code. */
 const char* flash_attn_status_str(fa_status status);

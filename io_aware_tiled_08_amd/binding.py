@@ -20,12 +20,13 @@ FA_F32, FA_F16, FA_BF16 = 0, 1, 2
 STATUS = {
     0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_HEAD_DIM",
     4: "FA_ERR_DTYPE", 5: "FA_ERR_ALIGN", 6: "FA_ERR_SCALE", 7: "FA_ERR_ALIAS",
-    8: "FA_ERR_NO_DEVICE", 9: "FA_ERR_ARCH", 10: "FA_ERR_HIP",
+    8: "FA_ERR_NO_DEVICE", 9: "FA_ERR_ARCH", 10: "FA_ERR_HIP", 11: "FA_ERR_WORKSPACE",
 }
 STATUS_CODE = {name: code for code, name in STATUS.items()}
-EXPORTS = ("flash_attn_fwd", "flash_attn_status_str", "flash_attn_last_error",
-           "flash_attn_abi_version")
-ABI_VERSION = 1
+EXPORTS = ("flash_attn_fwd", "flash_attn_fwd_kvcache", "flash_attn_kvcache_splits",
+           "flash_attn_kvcache_workspace_size", "flash_attn_status_str",
+           "flash_attn_last_error", "flash_attn_abi_version")
+ABI_VERSION = 2
 
 _lib = None
 _lock = threading.Lock()
@@ -56,6 +57,14 @@ def lib() -> ctypes.CDLL:
             L.flash_attn_fwd.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 4 + [
                 ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
             L.flash_attn_fwd.restype = ctypes.c_int
+            L.flash_attn_fwd_kvcache.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 + [
+                ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
+                ctypes.c_int, ctypes.c_void_p]
+            L.flash_attn_fwd_kvcache.restype = ctypes.c_int
+            L.flash_attn_kvcache_splits.argtypes = [ctypes.c_int64] * 5 + [ctypes.c_int]
+            L.flash_attn_kvcache_splits.restype = ctypes.c_int
+            L.flash_attn_kvcache_workspace_size.argtypes = [ctypes.c_int64] * 5 + [ctypes.c_int]
+            L.flash_attn_kvcache_workspace_size.restype = ctypes.c_int64
             L.flash_attn_status_str.argtypes = [ctypes.c_int]
             L.flash_attn_status_str.restype = ctypes.c_char_p
             L.flash_attn_last_error.argtypes = []
@@ -131,6 +140,89 @@ def flash_attn_fwd(q, k, v, o=None, lse=None, *, scale: Optional[float] = None,
         st = L.flash_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                               lse.data_ptr(), B, H, N, d, float(scale), int(bool(causal)),
                               code, s.cuda_stream)
+    if st != 0:
+        raise FlashAttnError(st, L.flash_attn_last_error().decode())
+    return o, lse
+
+
+def kvcache_splits(B: int, H: int, Nq: int, Nk: int, d: int, num_splits: int = 0) -> int:
+    """Key ranges flash_attn_fwd_kvcache uses for these sizes (C ABI)."""
+    return lib().flash_attn_kvcache_splits(B, H, Nq, Nk, d, num_splits)
+
+
+def kvcache_workspace_size(B: int, H: int, Nq: int, Nk: int, d: int,
+                           num_splits: int = 0) -> int:
+    """Workspace bytes flash_attn_fwd_kvcache needs for these sizes (C ABI)."""
+    return lib().flash_attn_kvcache_workspace_size(B, H, Nq, Nk, d, num_splits)
+
+
+def flash_attn_fwd_kvcache_ptr(q: int, k: int, v: int, o: int, lse: int, B: int, H: int,
+                               Nq: int, Nk: int, d: int, scale: float, causal: bool,
+                               num_splits: int, workspace: int, workspace_bytes: int,
+                               dtype: int, stream: int = 0) -> int:
+    """Raw call of the C entry point on integer addresses; returns the status."""
+    return lib().flash_attn_fwd_kvcache(q, k, v, o, lse, B, H, Nq, Nk, d, scale,
+                                        int(bool(causal)), num_splits, workspace,
+                                        workspace_bytes, dtype, stream)
+
+
+def flash_attn_fwd_kvcache(q, k, v, o=None, lse=None, *, scale: Optional[float] = None,
+                           causal: bool = False, num_splits: int = 0, workspace=None,
+                           stream=None) -> Tuple["object", "object"]:
+    """Attention of q [B, H, Nq, d] against a key/value cache k, v [B, H, Nk, d].
+
+    float16 or bfloat16 device tensors, contiguous.  causal: the queries are
+    the last Nq of Nk positions, query i sees keys j <= i + Nk - Nq.
+    num_splits <= 0 lets the library choose how many key ranges to compute
+    separately and merge.  workspace: optional device tensor of at least
+    kvcache_workspace_size(...) bytes; allocated here when needed and omitted.
+    o, lse: optional preallocated outputs.  Enqueued on `stream` (default: the
+    current stream of q's device) without synchronising.
+    """
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise ValueError(f"{name} must be a device tensor")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 4-d tensor")
+    B, H, Nq, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[1] != H or k.shape[3] != d:
+        raise ValueError("k and v must be [B, H, Nk, d] with q's B, H and d")
+    Nk = k.shape[2]
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k and v must have the same dtype")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k and v must be on the same device")
+    code = _dtype_code(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if o.shape != q.shape or o.dtype != q.dtype or o.device != q.device or not o.is_contiguous():
+        raise ValueError("o must be a contiguous tensor like q")
+    if (lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or lse.device != q.device
+            or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor on q's device")
+    L = lib()
+    need = L.flash_attn_kvcache_workspace_size(B, H, Nq, Nk, d, int(num_splits))
+    if need < 0:
+        raise ValueError("workspace size overflows")
+    ws_ptr, ws_bytes = 0, 0
+    if need > 0:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        if workspace.device != q.device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on q's device")
+        ws_ptr = workspace.data_ptr()
+        ws_bytes = workspace.numel() * workspace.element_size()
+    with torch.cuda.device(q.device):
+        s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        st = L.flash_attn_fwd_kvcache(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                      lse.data_ptr(), B, H, Nq, Nk, d, float(scale),
+                                      int(bool(causal)), int(num_splits), ws_ptr, ws_bytes,
+                                      code, s.cuda_stream)
     if st != 0:
         raise FlashAttnError(st, L.flash_attn_last_error().decode())
     return o, lse

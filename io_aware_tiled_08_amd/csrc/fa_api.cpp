@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <cstring>
 
+#include "fa_kvcache.h"
 #include "fa_launch.h"
 
 namespace {
@@ -62,6 +63,40 @@ fa_status check_device() {
     return fail(FA_ERR_ARCH, "device %d is %s; this library is built for gfx950", dev,
                 g_arch_name[dev]);
   return FA_OK;
+}
+
+// Split count and 32-key tiles per split for the key/value-cache path:
+// enough workgroups to give every CU of the MI355X (256) two of them, while
+// every wave keeps at least four tiles to stream; never more splits than
+// tiles or kKvMaxSplits.  `requested` > 0 overrides the first goal.
+struct KvSplit {
+  int n_split;
+  int tiles_per_split;
+};
+KvSplit kv_split(int64_t BH, int64_t Nq, int64_t Nk, int64_t d, int requested) {
+  const int64_t tiles = (Nk + fa::kKvKeys - 1) / fa::kKvKeys;
+  const int64_t blocks = BH * ((Nq + fa::kKvRows - 1) / fa::kKvRows);
+  int64_t S;
+  if (requested > 0) {
+    S = requested;
+  } else {
+    const int64_t want = (2 * 256 + blocks - 1) / (blocks > 0 ? blocks : 1);
+    const int64_t most = tiles / (4 * fa::kv_waves((int)d));
+    S = want < most ? want : most;
+  }
+  if (S > tiles) S = tiles;
+  if (S > fa::kKvMaxSplits) S = fa::kKvMaxSplits;
+  if (S < 1) S = 1;
+  const int64_t tps = (tiles + S - 1) / S;
+  KvSplit r;
+  r.tiles_per_split = (int)(tps > 0 ? tps : 1);
+  r.n_split = (int)((tiles + r.tiles_per_split - 1) / r.tiles_per_split);
+  if (r.n_split < 1) r.n_split = 1;
+  return r;
+}
+
+int64_t kv_workspace_bytes(int64_t BH, int64_t Nq, int64_t d, int n_split) {
+  return n_split > 1 ? (int64_t)n_split * BH * Nq * (d + 1) * 4 : 0;
 }
 
 }  // namespace
@@ -127,6 +162,103 @@ fa_status flash_attn_fwd(const void* q, const void* k, const void* v, void* o, f
   return FA_OK;
 }
 
+int flash_attn_kvcache_splits(int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d,
+                              int num_splits) {
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || (d != 64 && d != 128)) return 1;
+  if (B > ((int64_t)1 << 40) / H) return 1;
+  return kv_split(B * H, Nq, Nk, d, num_splits).n_split;
+}
+
+int64_t flash_attn_kvcache_workspace_size(int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                                          int64_t d, int num_splits) {
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || (d != 64 && d != 128)) return 0;
+  if (B > ((int64_t)1 << 40) / H || Nq > ((int64_t)1 << 40) / (B * H)) return -1;
+  const int S = kv_split(B * H, Nq, Nk, d, num_splits).n_split;
+  return kv_workspace_bytes(B * H, Nq, d, S);
+}
+
+fa_status flash_attn_fwd_kvcache(const void* q, const void* k, const void* v, void* o,
+                                 float* lse, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                                 int64_t d, float scale, int causal, int num_splits,
+                                 void* workspace, int64_t workspace_bytes, fa_dtype dtype,
+                                 void* stream) {
+  g_last_error[0] = '\0';
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0)
+    return fail(FA_ERR_SHAPE, "B, H, Nq, Nk must be >= 0 (got %lld, %lld, %lld, %lld)",
+                (long long)B, (long long)H, (long long)Nq, (long long)Nk);
+  if (d != 64 && d != 128) return fail(FA_ERR_HEAD_DIM, "d must be 64 or 128 (got %lld)", (long long)d);
+  if (dtype != FA_F16 && dtype != FA_BF16)
+    return fail(FA_ERR_DTYPE, "the key/value-cache path takes FA_F16 or FA_BF16 (got %d)", (int)dtype);
+  if (!std::isfinite(scale)) return fail(FA_ERR_SCALE, "scale must be finite");
+  if (B == 0 || H == 0 || Nq == 0) return FA_OK;
+  if (Nk == 0) return fail(FA_ERR_SHAPE, "Nk = 0: the queries see no key");
+  if (causal && Nk < Nq)
+    return fail(FA_ERR_SHAPE, "causal queries are the last Nq of Nk positions: need Nk >= Nq "
+                "(got Nq = %lld, Nk = %lld)", (long long)Nq, (long long)Nk);
+  if (!q || !k || !v || !o || !lse) return fail(FA_ERR_NULL, "q, k, v, o and lse must be non-NULL");
+  const uintptr_t mis = ((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse) & 15u;
+  if (mis) return fail(FA_ERR_ALIGN, "q, k, v, o and lse must be 16-byte aligned");
+
+  const int64_t elem = 2;
+  const int64_t kLimit = (int64_t)1 << 62;
+  const int64_t nmax = Nq > Nk ? Nq : Nk;
+  if (B > kLimit / H || nmax > kLimit / (B * H) || (d + 1) * elem * 2 > kLimit / (B * H * nmax))
+    return fail(FA_ERR_SHAPE, "B*H*N*d*elem overflows");
+  const int64_t BH = B * H;
+  const KvSplit sp = kv_split(BH, Nq, Nk, d, num_splits);
+  const int64_t nqb = (Nq + fa::kKvRows - 1) / fa::kKvRows;
+  if (BH * nqb > (int64_t)INT32_MAX / sp.n_split)
+    return fail(FA_ERR_SHAPE, "B*H*ceil(Nq/%d)*splits = %lld workgroups exceeds the grid limit",
+                fa::kKvRows, (long long)(BH * nqb * sp.n_split));
+  const int64_t need = kv_workspace_bytes(BH, Nq, d, sp.n_split);
+  if (need > 0) {
+    if (!workspace)
+      return fail(FA_ERR_WORKSPACE, "%d key splits need a workspace of %lld bytes", sp.n_split,
+                  (long long)need);
+    if ((uintptr_t)workspace & 15u) return fail(FA_ERR_ALIGN, "workspace must be 16-byte aligned");
+    if (workspace_bytes < need)
+      return fail(FA_ERR_WORKSPACE, "workspace has %lld bytes, %d key splits need %lld",
+                  (long long)workspace_bytes, sp.n_split, (long long)need);
+  }
+
+  const int64_t qbytes = BH * Nq * d * elem;
+  const int64_t kbytes = BH * Nk * d * elem;
+  const int64_t lbytes = BH * Nq * 4;
+  if (overlaps(o, qbytes, q, qbytes) || overlaps(o, qbytes, k, kbytes) ||
+      overlaps(o, qbytes, v, kbytes) || overlaps(lse, lbytes, q, qbytes) ||
+      overlaps(lse, lbytes, k, kbytes) || overlaps(lse, lbytes, v, kbytes) ||
+      overlaps(lse, lbytes, o, qbytes))
+    return fail(FA_ERR_ALIAS, "o and lse must not overlap q, k, v or each other");
+  if (need > 0 && (overlaps(workspace, need, q, qbytes) || overlaps(workspace, need, k, kbytes) ||
+                   overlaps(workspace, need, v, kbytes) || overlaps(workspace, need, o, qbytes) ||
+                   overlaps(workspace, need, lse, lbytes)))
+    return fail(FA_ERR_ALIAS, "the workspace must not overlap q, k, v, o or lse");
+
+  fa_status st = check_device();
+  if (st != FA_OK) return st;
+
+  fa::KvArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.workspace = need > 0 ? workspace : nullptr;
+  a.BH = BH;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.d = (int)d;
+  a.scale = scale;
+  a.causal = causal != 0;
+  a.dtype = (fa::Dtype)dtype;
+  a.n_split = sp.n_split;
+  a.tiles_per_split = sp.tiles_per_split;
+  (void)hipGetLastError();
+  const hipError_t e = fa::launch_kvcache(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
 const char* flash_attn_status_str(fa_status s) {
   switch (s) {
     case FA_OK: return "FA_OK: success";
@@ -140,6 +272,7 @@ const char* flash_attn_status_str(fa_status s) {
     case FA_ERR_NO_DEVICE: return "FA_ERR_NO_DEVICE: no usable HIP device";
     case FA_ERR_ARCH: return "FA_ERR_ARCH: device is not gfx950";
     case FA_ERR_HIP: return "FA_ERR_HIP: HIP runtime error";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
   }
   return "unknown fa_status";
 }

@@ -1,0 +1,145 @@
+// Device helpers shared by the fp16/bf16 kernels (the square forward kernel
+// and the key/value-cache kernel): MFMA wrappers per input type, the LDS
+// chunk permutation, transposing LDS reads, direct-to-LDS buffer loads,
+// register fences and a max tree.
+#pragma once
+
+#include "fa_device.h"
+
+namespace fa {
+namespace {
+
+// Largest excess (log2 units) of a score over the reference maximum before
+// the accumulator is rescaled: weights stay <= 2^8 = 256, far inside the
+// fp16/bf16 range and exact-ratio in fp32.
+constexpr float kRescaleSlack = 8.0f;
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+template <typename T>
+struct Half;
+
+template <>
+struct Half<_Float16> {
+  using Frag = f16x8;
+  using Pair = f16x2;
+  static __device__ __forceinline__ f32x16 mma(Frag a, Frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  // Round-to-nearest-even pair conversion (v_cvt_pk_f16_f32).
+  static __device__ __forceinline__ Pair pack(float x, float y) {
+    return __builtin_convertvector((f32x2){x, y}, Pair);
+  }
+  // acc + p.x + p.y in fp32 (v_dot2 with ones)
+  static __device__ __forceinline__ float sum2(Pair p, float acc) {
+    const Pair one = {(_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_fdot2(p, one, acc, false);
+  }
+};
+
+template <>
+struct Half<__bf16> {
+  using Frag = bf16x8;
+  using Pair = bf16x2;
+  static __device__ __forceinline__ f32x16 mma(Frag a, Frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  // Round-to-nearest-even pair conversion (v_cvt_pk_bf16_f32).
+  static __device__ __forceinline__ Pair pack(float x, float y) {
+    return __builtin_convertvector((f32x2){x, y}, Pair);
+  }
+  static __device__ __forceinline__ float sum2(Pair p, float acc) {
+    const Pair one = {(__bf16)1.0f, (__bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(p, one, acc, false);
+  }
+};
+
+// Position of 16-byte chunk c of row r inside the LDS row (rows are 2*D bytes,
+// LDS banks repeat every 256 bytes = 16 chunks).  Each map is an XOR with a
+// row-dependent mask, so it is its own inverse.
+//   K is read as MFMA A rows: 16 lanes read one chunk of 16 different rows
+//   (rows distinct mod 16), so those must land in 16 different bank groups.
+//   V is read by transposing loads: 32 lanes read 4 chunks of 4 consecutive
+//   rows (first row a multiple of 4); those 16 chunks must not collide.
+template <int D>
+struct Swizzle {
+  static_assert(D == 64 || D == 128, "head dim");
+  static __device__ __forceinline__ constexpr int k(int r, int c) {
+    return D == 128 ? c ^ (r & 15) : c ^ ((r >> 1) & 7);
+  }
+  static __device__ __forceinline__ constexpr int v(int r, int c) {
+    return D == 128 ? c ^ ((r & 3) << 2) : c ^ (((r >> 1) & 1) << 2);
+  }
+};
+
+typedef short s16x4 __attribute__((vector_size(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, output lane i, element
+// e receives element i%4 of the 4 elements addressed by lane 4*e + i/4.  When
+// lane j of the group addresses row r0 + j/4, columns c0 + 4*(j%4) .. +3 of a
+// row-major 16-bit matrix, output lane i receives column c0 + i of rows
+// r0 .. r0+3, i.e. a transposed 4 x 16 block.
+__device__ __forceinline__ u32x2 lds_read_tr(const char* base, int byte_off) {
+  lds_s16x4* ptr = (lds_s16x4*)((lds_char*)const_cast<char*>(base) + byte_off);
+  return bits<u32x2>(__builtin_amdgcn_ds_read_tr16_b64_v4i16(ptr));
+}
+
+// Raw buffer resource over [base, base + bytes): buffer loads at offsets
+// >= bytes return zeros.  Dword 3 is the gfx9 raw-buffer format word.
+__device__ __forceinline__ u32x4 buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  return u32x4{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
+}
+
+// buffer_load_dwordx4 ... lds: lane i copies the 16 bytes at buffer offset
+// voff into LDS bytes lds + 16*i .. +15.  Issued from inline assembly so that
+// the compiler's wait-count pass does not make every later LDS read wait for
+// these loads (it cannot tell the double buffers apart); the kernel waits for
+// them itself (vmcnt(0) + barrier) before the first read of the buffer.  M0
+// holds the LDS base; nothing else in these kernels uses M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma_load16(u32x4 rsrc, uint32_t lds, int voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_char*)const_cast<void*>(p);
+}
+
+// Register fences.  The compiler may move plain arithmetic across
+// s_barrier (only memory effects are ordered by it); an empty volatile asm
+// that reads and rewrites a value pins the computation of that value before
+// the fence and every later use after it, which keeps each phase's work
+// inside its slot.
+template <typename V>
+__device__ __forceinline__ void fence(V& x) {
+  asm volatile("" : "+v"(x));
+}
+
+// Maximum of n values get(0..n-1) as a balanced tree of three-input maxima
+// (v_max3_f32), so the dependency chain is log3(n) deep instead of n.
+template <int n, typename Get>
+__device__ __forceinline__ float tree_max(Get get) {
+  if constexpr (n == 1) {
+    return get(0);
+  } else if constexpr (n == 2) {
+    return fmaxf(get(0), get(1));
+  } else {
+    constexpr int a = (n + 2) / 3, b = (n - a + 1) / 2, c = n - a - b;
+    const float x = tree_max<a>(get);
+    const float y = tree_max<b>([&](int i) { return get(a + i); });
+    const float z = tree_max<c>([&](int i) { return get(a + b + i); });
+    return fmaxf(fmaxf(x, y), z);
+  }
+}
+
+}  // namespace
+}  // namespace fa

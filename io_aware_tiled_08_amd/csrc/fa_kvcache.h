@@ -1,0 +1,41 @@
+// Internal interface between the C ABI layer (fa_api.cpp) and the
+// key/value-cache kernels (fa_fwd_kvcache.hip).  Not installed, not part of
+// the ABI.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include "fa_launch.h"
+
+namespace fa {
+
+constexpr int kKvRows = 32;        // query rows per workgroup
+constexpr int kKvKeys = 32;        // keys per tile
+constexpr int kKvMaxSplits = 256;  // most key ranges one call may use
+
+struct KvArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  void* workspace;  // n_split * BH * Nq * (d + 1) floats when n_split > 1
+  int64_t BH;       // B * H
+  int64_t Nq;
+  int64_t Nk;
+  int d;
+  float scale;
+  bool causal;
+  Dtype dtype;
+  int n_split;          // key ranges, >= 1
+  int tiles_per_split;  // 32-key tiles per range
+};
+
+// Waves per workgroup of the cache kernel at head dimension d.
+inline int kv_waves(int d) { return d == 128 ? 4 : 8; }
+
+// Enqueue the cache kernel (and, with n_split > 1, the merge kernel).
+hipError_t launch_kvcache(const KvArgs& a, hipStream_t stream);  // FA_F16, FA_BF16
+
+}  // namespace fa

@@ -94,6 +94,74 @@ WORKLOADS = {
 HEADLINE = "headline_f16_d128"
 
 
+@dataclasses.dataclass(frozen=True)
+class CacheWorkload:
+    """New queries against a key/value cache: Q is [B, H, Nq, d], K and V
+    [B, H, Nk, d]; causal queries are the last Nq of Nk positions."""
+
+    name: str
+    seed: int
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    d: int
+    dtype: str
+    causal: bool
+    description: str = ""
+
+    @property
+    def scale(self) -> float:
+        return default_scale(self.d)
+
+    def visible_keys(self) -> int:
+        """Query-key pairs of one head that the mask lets through."""
+        if not self.causal:
+            return self.Nq * self.Nk
+        off = self.Nk - self.Nq
+        return sum(min(self.Nk, i + 1 + off) for i in range(self.Nq))
+
+    def flops(self) -> float:
+        """Matrix-product FLOPs: 4*d per visible query-key pair."""
+        return 4.0 * self.B * self.H * self.visible_keys() * self.d
+
+    def compulsory_bytes(self) -> int:
+        """Read Q, K, V once, write O and the fp32 LSE once."""
+        e = ELEM_BYTES[self.dtype]
+        return (2 * self.B * self.H * self.Nq * self.d * e + 2 * self.B * self.H * self.Nk * self.d * e
+                + 4 * self.B * self.H * self.Nq)
+
+
+# Decode against a cache: a batch of single-token queries over an 8k cache, and
+# a 16-token causal step (e.g. speculative decoding) over a 128k-token cache at
+# batch 1.  Bound by reading K and V from HBM.
+CACHE_WORKLOADS = {
+    "decode_f16_d128": CacheWorkload(
+        "decode_f16_d128", 6, 16, 16, 1, 8192, 128, "f16", False,
+        description="B=16 H=16 Nq=1 Nk=8192 d=128 fp16, N(0,1)"),
+    "decode_long_bf16": CacheWorkload(
+        "decode_long_bf16", 7, 1, 8, 16, 131072, 128, "bf16", True,
+        description="B=1 H=8 Nq=16 Nk=131072 d=128 bf16, N(0,1), causal "
+                    "(queries are the last 16 positions)"),
+}
+
+
+def random_cache_inputs(B: int, H: int, Nq: int, Nk: int, d: int, dtype: str, seed: int):
+    """Q [B, H, Nq, d] and K, V [B, H, Nk, d], iid N(0,1), same recipe as
+    random_qkv (tensor ids 0, 1, 2)."""
+    def normal(n):
+        return lambda rng, b, h: rng.standard_normal((n, d), dtype=np.float32)
+
+    q = _draw(seed, TENSOR_Q, B, H, Nq, d, dtype, normal(Nq))
+    k = _draw(seed, TENSOR_K, B, H, Nk, d, dtype, normal(Nk))
+    v = _draw(seed, TENSOR_V, B, H, Nk, d, dtype, normal(Nk))
+    return q, k, v
+
+
+def cache_workload_inputs(w: CacheWorkload):
+    return random_cache_inputs(w.B, w.H, w.Nq, w.Nk, w.d, w.dtype, w.seed)
+
+
 def default_scale(d: int) -> float:
     """1/sqrt(d), rounded to float32: the value the kernel receives."""
     return float(np.float32(1.0 / math.sqrt(d)))

@@ -153,3 +153,114 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(binding, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         binding.lib()
+
+
+# ---- flash_attn_fwd_kvcache: argument checks before any HIP call ----------
+WS = 0x10000000000 + 5 * 64 * GiB
+
+
+def _kv(L, q=Q, k=K, v=V, o=O, lse=LSE, B=2, H=3, Nq=4, Nk=1000, d=64, scale=0.125,
+        causal=0, splits=0, ws=WS, ws_bytes=1 << 30, dtype=1):
+    st = L.flash_attn_fwd_kvcache(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, splits,
+                                  ws, ws_bytes, dtype, None)
+    return st, L.flash_attn_last_error().decode()
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "o", "lse"])
+def test_kv_null_pointer(L, field):
+    st, msg = _kv(L, **{field: None})
+    assert st == 1 and "non-NULL" in msg
+
+
+@pytest.mark.parametrize("shape", [(-1, 1, 1, 1), (1, -1, 1, 1), (1, 1, -1, 1), (1, 1, 1, -1)])
+def test_kv_negative_shape(L, shape):
+    B, H, Nq, Nk = shape
+    assert _kv(L, B=B, H=H, Nq=Nq, Nk=Nk)[0] == 2
+
+
+def test_kv_no_keys_and_short_causal_cache(L):
+    st, msg = _kv(L, Nk=0)
+    assert st == 2 and "no key" in msg
+    st, msg = _kv(L, Nq=10, Nk=9, causal=1)
+    assert st == 2 and "Nk >= Nq" in msg
+    # non-causal queries may outnumber the keys
+    assert _kv(L, Nq=10, Nk=9, causal=0)[0] not in (2,)
+
+
+@pytest.mark.parametrize("dtype", [0, 3, -1])
+def test_kv_dtype(L, dtype):
+    st, msg = _kv(L, dtype=dtype)
+    assert st == 4
+    if dtype == 0:
+        assert "FA_F16 or FA_BF16" in msg
+
+
+@pytest.mark.parametrize("d", [0, 32, 96, 256])
+def test_kv_head_dim(L, d):
+    assert _kv(L, d=d)[0] == 3
+
+
+@pytest.mark.parametrize("scale", [math.inf, -math.inf, math.nan])
+def test_kv_scale(L, scale):
+    assert _kv(L, scale=scale)[0] == 6
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "o", "lse", "ws"])
+def test_kv_misaligned(L, field):
+    base = {"q": Q, "k": K, "v": V, "o": O, "lse": LSE, "ws": WS}[field]
+    assert _kv(L, splits=4, **{field: base + 8})[0] == 5
+
+
+def test_kv_empty_is_a_no_op(L):
+    for B, H, Nq in [(0, 3, 4), (2, 0, 4), (2, 3, 0)]:
+        assert _kv(L, B=B, H=H, Nq=Nq, q=None, o=None, lse=None, ws=None) == (0, "")
+
+
+def test_kv_split_count_and_workspace_size(L):
+    # one head, one query, 32768 keys: the library splits the keys
+    S = L.flash_attn_kvcache_splits(1, 1, 1, 32768, 128, 0)
+    assert 1 < S <= 256
+    assert L.flash_attn_kvcache_workspace_size(1, 1, 1, 32768, 128, 0) == S * 1 * 1 * 129 * 4
+    # a requested count is honoured up to the number of 32-key tiles
+    assert L.flash_attn_kvcache_splits(1, 1, 1, 32768, 128, 7) == 7
+    assert L.flash_attn_kvcache_splits(1, 1, 1, 100, 128, 50) == 4
+    assert L.flash_attn_kvcache_splits(1, 1, 1, 100, 128, 1) == 1
+    assert L.flash_attn_kvcache_workspace_size(1, 1, 1, 100, 128, 1) == 0
+    # many heads already fill the GPU: no split
+    assert L.flash_attn_kvcache_splits(64, 32, 64, 512, 128, 0) == 1
+    # invalid sizes need nothing
+    assert L.flash_attn_kvcache_workspace_size(0, 1, 1, 100, 64, 0) == 0
+    assert L.flash_attn_kvcache_splits(1, 1, 1, 100, 96, 0) == 1
+    # every tile of every split count lands in exactly one split
+    for nk in (1, 31, 32, 33, 1000, 4097):
+        for req in (1, 2, 3, 5, 64, 300):
+            S = L.flash_attn_kvcache_splits(1, 1, 1, nk, 64, req)
+            tiles = -(-nk // 32)
+            assert 1 <= S <= min(tiles, 256)
+
+
+def test_kv_workspace_missing_or_small(L):
+    need = L.flash_attn_kvcache_workspace_size(2, 3, 4, 1000, 64, 4)
+    assert need == 4 * 2 * 3 * 4 * 65 * 4
+    st, msg = _kv(L, splits=4, ws=None)
+    assert st == 11 and "workspace" in msg
+    st, msg = _kv(L, splits=4, ws_bytes=need - 1)
+    assert st == 11
+    # one split needs no workspace at all
+    st, msg = _kv(L, splits=1, ws=None, ws_bytes=0)
+    assert st not in (11, 1), msg
+
+
+def test_kv_alias(L):
+    assert _kv(L, o=Q)[0] == 7
+    assert _kv(L, lse=K + 64)[0] == 7
+    assert _kv(L, splits=4, ws=O)[0] == 7
+    assert _kv(L, splits=4, ws=LSE)[0] == 7
+
+
+def test_kv_no_device_reported_not_crashed(L):
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    st, msg = _kv(L, splits=4)
+    assert st == 8, msg
