@@ -40,27 +40,49 @@ if ROOT not in sys.path:
 MFMA_PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3}
 HBM_PEAK_GBPS = 8000.0
 PEAK_CLOCK_MHZ = 2400.0  # the engine clock the published MFMA peaks are quoted at
+_CSRC = os.path.join(ROOT, "io_aware_tiled_08_amd", "csrc")
+# Source files each kernel is compiled from (its .hip and the headers it includes).
 KERNEL_SOURCES = {
-    "f16": os.path.join(ROOT, "io_aware_tiled_08_amd", "csrc", "fa_fwd_f16.hip"),
-    "bf16": os.path.join(ROOT, "io_aware_tiled_08_amd", "csrc", "fa_fwd_f16.hip"),
-    "f32": os.path.join(ROOT, "io_aware_tiled_08_amd", "csrc", "fa_fwd_f32.hip"),
+    "f16": ("fa_fwd_f16.hip", "fa_f16_common.h", "fa_device.h"),
+    "bf16": ("fa_fwd_f16.hip", "fa_f16_common.h", "fa_device.h"),
+    "f32": ("fa_fwd_f32.hip", "fa_device.h"),
+    "kvcache": ("fa_fwd_kvcache.hip", "fa_f16_common.h", "fa_device.h"),
 }
-KERNEL_NAME_PATTERN = {"f16": "fwd_f16_kernel", "bf16": "fwd_f16_kernel", "f32": "fwd_f32_kernel"}
+# (dominant kernel, every kernel of one call) name patterns in rocprofv3 output
+KERNEL_NAME_PATTERN = {"f16": ("fwd_f16_kernel", "fwd_f16_kernel"),
+                       "bf16": ("fwd_f16_kernel", "fwd_f16_kernel"),
+                       "f32": ("fwd_f32_kernel", "fwd_f32_kernel"),
+                       "kvcache": ("kvcache_fwd_kernel", "kvcache_")}
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 512 << 20  # one calibration copy: 512 MiB read + 512 MiB written
 COPY_REPS = 3
 
 
-def kernel_source_digest(dtype: str) -> str:
-    with open(KERNEL_SOURCES[dtype], "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+def kernel_source_digest(key: str) -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[key]:
+        with open(os.path.join(_CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def workload_by_name(name: str):
+    """(workload, kernel key) for a square or a key/value-cache workload."""
+    from io_aware_tiled_08_amd import workloads as W
+    if name in W.WORKLOADS:
+        w = W.WORKLOADS[name]
+        return w, w.dtype
+    if name in W.CACHE_WORKLOADS:
+        return W.CACHE_WORKLOADS[name], "kvcache"
+    raise SystemExit(f"unknown workload {name!r}; known: "
+                     f"{sorted(W.WORKLOADS) + sorted(W.CACHE_WORKLOADS)}")
 
 
 def traffic_path(workload: str) -> str:
     return os.path.join(PROFILES, f"traffic_{workload}.md")
 
 
-def measured_traffic(workload: str, dtype: str):
+def measured_traffic(workload: str, key: str):
     """HBM bytes per launch from the committed counter summary, or None when
     there is none or the kernel source changed since it was taken."""
     path = traffic_path(workload)
@@ -69,7 +91,7 @@ def measured_traffic(workload: str, dtype: str):
     text = open(path).read()
     sha = re.search(r"^kernel_source_sha256:\s*([0-9a-f]{64})\s*$", text, re.M)
     val = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)\s*$", text, re.M)
-    if not sha or not val or sha.group(1) != kernel_source_digest(dtype):
+    if not sha or not val or sha.group(1) != kernel_source_digest(key):
         return None
     return float(val.group(1))
 
@@ -136,22 +158,22 @@ def summarize_traffic(fetch_csv: str, write_csv: str, workload: str) -> str:
     dispatch) of `bench.py --copy-calibration` into HBM bytes per launch of
     the attention kernel, scaled by what the same counters read for the
     calibration copies, and writes profiles/traffic_<workload>.md."""
-    from io_aware_tiled_08_amd import workloads as W
-    w = W.WORKLOADS[workload]
-    pat = KERNEL_NAME_PATTERN[w.dtype]
+    w, key = workload_by_name(workload)
+    main_pat, all_pat = KERNEL_NAME_PATTERN[key]
     out = {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = _counter_rows(path, counter)
-        fa = [v for n, v in rows if pat in n]
+        calls = [v for n, v in rows if main_pat in n]
+        fa = [v for n, v in rows if all_pat in n]
         cp = [v for n, v in rows if "copy" in n.lower() or "elementwise" in n.lower()]
         cp = [v for v in cp if v > 0.5 * COPY_BYTES / 1024]  # the 512 MiB copies only
-        if not fa or not cp:
-            raise SystemExit(f"{path}: no {counter} rows for the kernel ({len(fa)}) or the copy ({len(cp)})")
+        if not calls or not cp:
+            raise SystemExit(f"{path}: no {counter} rows for the kernel ({len(calls)}) or the copy ({len(cp)})")
         copy_kib = sum(cp) / len(cp)
         factor = (COPY_BYTES / 1024) / copy_kib
-        fa_kib = sum(fa) / len(fa)
+        fa_kib = sum(fa) / len(calls)  # every kernel of one call, per call
         out[counter] = {"kernel_kib": fa_kib, "copy_kib": copy_kib, "factor": factor,
-                        "bytes": fa_kib * 1024 * factor, "n": len(fa)}
+                        "bytes": fa_kib * 1024 * factor, "n": len(calls)}
     total = out["FETCH_SIZE"]["bytes"] + out["WRITE_SIZE"]["bytes"]
     comp = w.compulsory_bytes()
     os.makedirs(PROFILES, exist_ok=True)
@@ -159,7 +181,8 @@ def summarize_traffic(fetch_csv: str, write_csv: str, workload: str) -> str:
         f"# HBM traffic of the forward kernel, workload {workload}",
         "",
         f"Workload: {w.description}.  Compulsory bytes (Q, K, V read once; O and fp32 LSE",
-        f"written once): {comp} ({comp / 2**20:.2f} MiB).",
+        f"written once): {comp} ({comp / 2**20:.2f} MiB).  Kernels counted per call: "
+        f"`{all_pat}*` (dispatches of `{main_pat}` = calls).",
         "",
         "Commands (GPU host, from the repository root):",
         "",
@@ -171,7 +194,7 @@ def summarize_traffic(fetch_csv: str, write_csv: str, workload: str) -> str:
         "        gpurun_out/traffic_" + workload + "/fetch/fetch_counter_collection.csv \\",
         "        gpurun_out/traffic_" + workload + "/write/write_counter_collection.csv",
         "",
-        "| counter | kernel KiB/dispatch (mean) | dispatches | 512 MiB copy reads as KiB | scale factor | bytes/launch |",
+        "| counter | kernel KiB/call (mean) | calls | 512 MiB copy reads as KiB | scale factor | bytes/call |",
         "|---|---|---|---|---|---|",
     ]
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
@@ -187,7 +210,7 @@ def summarize_traffic(fetch_csv: str, write_csv: str, workload: str) -> str:
         "kernel source hash matches):",
         "",
         f"hbm_bytes_per_launch: {total:.0f}",
-        f"kernel_source_sha256: {kernel_source_digest(w.dtype)}",
+        f"kernel_source_sha256: {kernel_source_digest(key)}",
         "",
     ]
     path = traffic_path(workload)
@@ -273,6 +296,41 @@ class ClockSampler:
         return v[len(v) // 2]
 
 
+def cpu_baseline_cache(w, q, k, v, budget_s: float):
+    """Times the fp64 oracle on a key/value-cache workload, one (b, h) head at
+    a time until the budget is spent (at least one head); the rate is the
+    compulsory bytes of the heads done per second, like the GPU figure."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                       if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    heads = 0
+    t0 = time.perf_counter()
+    for b in range(w.B):
+        for h in range(w.H):
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            oracle.attention_forward(q[sl], k[sl], v[sl], w.scale, w.causal)
+            heads += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        else:
+            continue
+        break
+    el = time.perf_counter() - t0
+    done_bytes = w.compulsory_bytes() * heads / (w.B * w.H)
+    return {
+        "value": done_bytes / el / 1e9,
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{heads} of {w.B * w.H} (b,h) heads of {w.name}, all {w.Nq} query rows "
+                  f"each, fp64 numpy, {el:.1f} s",
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -300,24 +358,38 @@ def main():
               "shards by (batch, head) with no communication, and this build measures "
               "one GPU's share.", file=sys.stderr)
         sys.exit(2)
+    w, key = workload_by_name(name)
+    cache = key == "kvcache"
 
     import torch
 
-    from io_aware_tiled_08_amd import binding, flash_attn_fwd
+    from io_aware_tiled_08_amd import binding, flash_attn_fwd, flash_attn_fwd_kvcache
     if not os.path.exists(binding.library_path()):
         from io_aware_tiled_08_amd.build import build_library
         build_library()
 
-    w = W.WORKLOADS[name]
-    q, k, v = W.workload_inputs(w)
     dev = torch.device("cuda:0")
-    qd, kd, vd = (x.to(dev) for x in (q, k, v))
-    o = torch.empty_like(qd)
-    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
+    if cache:
+        q, k, v = W.cache_workload_inputs(w)
+        qd, kd, vd = (x.to(dev) for x in (q, k, v))
+        o = torch.empty_like(qd)
+        lse = torch.empty((w.B, w.H, w.Nq), dtype=torch.float32, device=dev)
+        n_split = binding.kvcache_splits(w.B, w.H, w.Nq, w.Nk, w.d, 0)
+        ws_bytes = binding.kvcache_workspace_size(w.B, w.H, w.Nq, w.Nk, w.d, 0)
+        ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
 
-    def step():
-        flash_attn_fwd(qd, kd, vd, o, lse, scale=w.scale, causal=w.causal, stream=stream)
+        def step():
+            flash_attn_fwd_kvcache(qd, kd, vd, o, lse, scale=w.scale, causal=w.causal,
+                                   workspace=ws, stream=stream)
+    else:
+        q, k, v = W.workload_inputs(w)
+        qd, kd, vd = (x.to(dev) for x in (q, k, v))
+        o = torch.empty_like(qd)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+
+        def step():
+            flash_attn_fwd(qd, kd, vd, o, lse, scale=w.scale, causal=w.causal, stream=stream)
 
     if args.warmup is None:
         warmup = 0
@@ -332,7 +404,7 @@ def main():
         for _ in range(warmup):
             step()
     torch.cuda.synchronize()
-    # HIP events recorded on the stream the kernel is launched on.
+    # HIP events recorded on the stream the kernels are launched on.
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -342,10 +414,10 @@ def main():
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = start.elapsed_time(end) / args.steps  # one launch per step
+    ms = start.elapsed_time(end) / args.steps  # one call per step
 
-    # Per-launch distribution: one event pair around each launch, after the
-    # timed region (so the extra event records do not perturb it), with the
+    # Per-call distribution: one event pair around each call, after the timed
+    # region (so the extra event records do not perturb it), with the
     # graphics clock sampled meanwhile.
     n_dist = min(args.steps, max(20, int(2.0 / max(ms * 1e-3, 1e-6))))
     pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -370,51 +442,91 @@ def main():
 
     flops = w.flops()
     tflops = flops / (ms * 1e-3) / 1e12
-    peak = MFMA_PEAK_TFLOPS[w.dtype]
-    traffic = measured_traffic(name, w.dtype)
-    roofline = {
-        "bound": "mfma",
-        "achieved": round(tflops, 2),
-        "peak": peak,
-        "unit": "TFLOP/s",
-        "frac": round(tflops / peak, 4),
-        "traffic": traffic,
-        "kernel_ms": round(ms, 5),
-        "compulsory_bytes": w.compulsory_bytes(),
-        "compulsory_GBps": round(w.compulsory_bytes() / (ms * 1e-3) / 1e9, 1),
-        "compulsory_frac_of_hbm_peak": round(w.compulsory_bytes() / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-        "launch_ms_p10_p50_p90": [round(percentile(per_launch, f), 5) for f in (0.1, 0.5, 0.9)],
-        "launches_sampled": len(per_launch),
-    }
-    mhz = clock.median_mhz()
-    if mhz:
-        # The same kernel against the peak at the clock the card actually ran.
-        peak_at_clock = peak * mhz / PEAK_CLOCK_MHZ
-        roofline["gfx_clock_mhz_median"] = round(mhz, 1)
-        roofline["frac_at_measured_clock"] = round(tflops / peak_at_clock, 4)
+    comp = w.compulsory_bytes()
+    gbps = comp / (ms * 1e-3) / 1e9
+    traffic = measured_traffic(name, key)
+    dist = [round(percentile(per_launch, f), 5) for f in (0.1, 0.5, 0.9)]
     props = torch.cuda.get_device_properties(dev)
-    result = {
-        "metric": "attention fwd TFLOP/s and % of MFMA peak, N=4096 d=128 fp16 (1 GPU)",
-        "value": round(tflops, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": warmup,
-        "ms_per_step": round(ms, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": w.dtype,
-        "data": "synthetic",
-        "config": {"workload": name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
-                   "causal": w.causal, "inputs": w.description},
-        "roofline": roofline,
-        "device": {"name": props.name, "cus": props.multi_processor_count,
-                   "arch": getattr(props, "gcnArchName", "")},
-        "timed_wall_s": round(wall, 4),
-    }
+    mhz = clock.median_mhz()
+    if cache:
+        # Reading the cache from HBM bounds this path: GB/s against HBM peak.
+        roofline = {
+            "bound": "hbm",
+            "achieved": round(gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(gbps / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "kernel_ms": round(ms, 5),
+            "kernels_per_call": 1 if n_split == 1 else 2,
+            "key_splits": n_split,
+            "compulsory_bytes": comp,
+            "tflops": round(tflops, 2),
+            "launch_ms_p10_p50_p90": dist,
+            "launches_sampled": len(per_launch),
+        }
+        if mhz:
+            roofline["gfx_clock_mhz_median"] = round(mhz, 1)
+        result = {
+            "metric": "attention decode against a K/V cache: GB/s of compulsory HBM bytes (1 GPU)",
+            "value": round(gbps, 1),
+            "unit": "GB/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": warmup,
+            "ms_per_step": round(ms, 5),
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": w.dtype,
+            "data": "synthetic",
+            "config": {"workload": name, "B": w.B, "H": w.H, "Nq": w.Nq, "Nk": w.Nk, "d": w.d,
+                       "causal": w.causal, "inputs": w.description},
+            "roofline": roofline,
+        }
+    else:
+        peak = MFMA_PEAK_TFLOPS[w.dtype]
+        roofline = {
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / peak, 4),
+            "traffic": traffic,
+            "kernel_ms": round(ms, 5),
+            "compulsory_bytes": comp,
+            "compulsory_GBps": round(gbps, 1),
+            "compulsory_frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+            "launch_ms_p10_p50_p90": dist,
+            "launches_sampled": len(per_launch),
+        }
+        if mhz:
+            # The same kernel against the peak at the clock the card actually ran.
+            roofline["gfx_clock_mhz_median"] = round(mhz, 1)
+            roofline["frac_at_measured_clock"] = round(tflops / (peak * mhz / PEAK_CLOCK_MHZ), 4)
+        result = {
+            "metric": "attention fwd TFLOP/s and % of MFMA peak, N=4096 d=128 fp16 (1 GPU)",
+            "value": round(tflops, 2),
+            "unit": "TFLOP/s",
+            "n_gpus": 1,
+            "steps": args.steps,
+            "warmup": warmup,
+            "ms_per_step": round(ms, 5),
+            "higher_is_better": True,
+            "scaling": "weak",
+            "vs_baseline": None,
+            "dtype": w.dtype,
+            "data": "synthetic",
+            "config": {"workload": name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                       "causal": w.causal, "inputs": w.description},
+            "roofline": roofline,
+        }
+    result["device"] = {"name": props.name, "cus": props.multi_processor_count,
+                        "arch": getattr(props, "gcnArchName", "")}
+    result["timed_wall_s"] = round(wall, 4)
     if args.cpu_budget > 0:
-        result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)
+        result["cpu_baseline"] = (cpu_baseline_cache(w, q, k, v, args.cpu_budget) if cache
+                                  else cpu_baseline(w, q, k, v, args.cpu_budget))
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

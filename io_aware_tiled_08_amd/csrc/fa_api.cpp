@@ -128,7 +128,8 @@ fa_status flash_attn_fwd(const void* q, const void* k, const void* v, void* o, f
   const int64_t BH = B * H;
   const int br = fa::rows_per_workgroup((fa::Dtype)dtype);
   const int64_t n_qblk = (N + br - 1) / br;
-  if (n_qblk > INT32_MAX || BH * n_qblk > (int64_t)INT32_MAX)
+  const int64_t tpw = fa::threads_per_workgroup((fa::Dtype)dtype, (int)d);
+  if (n_qblk > INT32_MAX || BH * n_qblk > (int64_t)UINT32_MAX / tpw)
     return fail(FA_ERR_SHAPE, "B*H*ceil(N/%d) = %lld workgroups exceeds the grid limit", br,
                 (long long)(BH * n_qblk));
 
@@ -207,7 +208,9 @@ fa_status flash_attn_fwd_kvcache(const void* q, const void* k, const void* v, vo
   const int64_t BH = B * H;
   const KvSplit sp = kv_split(BH, Nq, Nk, d, num_splits);
   const int64_t nqb = (Nq + fa::kKvRows - 1) / fa::kKvRows;
-  if (BH * nqb > (int64_t)INT32_MAX / sp.n_split)
+  const int64_t kv_tpw = fa::kv_waves((int)d) * 64;
+  if (BH * nqb > (int64_t)UINT32_MAX / kv_tpw / sp.n_split ||
+      (sp.n_split > 1 && BH * Nq > (int64_t)UINT32_MAX / 256))
     return fail(FA_ERR_SHAPE, "B*H*ceil(Nq/%d)*splits = %lld workgroups exceeds the grid limit",
                 fa::kKvRows, (long long)(BH * nqb * sp.n_split));
   const int64_t need = kv_workspace_bytes(BH, Nq, d, sp.n_split);

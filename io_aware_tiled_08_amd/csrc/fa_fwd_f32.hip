@@ -224,6 +224,7 @@ __global__ void __launch_bounds__(F32Lds<D>::kWaves * 64, 1) fwd_f32_kernel(Kern
 template <int D, bool CAUSAL>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   static_assert(kRows == kRowsPerWorkgroupF32, "rows per workgroup");
+  if (threads_per_workgroup(Dtype::F32, D) != F32Lds<D>::kWaves * 64) return hipErrorInvalidConfiguration;
   KernelParams p;
   p.q = a.q;
   p.k = a.k;

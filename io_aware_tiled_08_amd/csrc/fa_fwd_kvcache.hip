@@ -18,7 +18,7 @@
 //     32-query block, split), so that a single head at batch 1 still fills
 //     the GPU;
 //   * inside a workgroup every wave walks its own 32-key tiles (wave w takes
-//     every NW-th tile of the range) through its own double buffer in LDS,
+//     every NW-th tile of the range) through its own LDS stages (kv_bufs),
 //     filled by buffer_load ... lds one tile ahead and waited for with the
 //     wave's own vmcnt, so waves never wait for each other in the loop;
 //   * per tile: S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_32x32x16 (query
@@ -56,21 +56,13 @@ struct KvParams {
   uint32_t q_sign;  // XOR mask flipping Q's sign when scale < 0
 };
 
-// Waves per workgroup: every wave owns 2 buffers x (K + V) x 32 rows x 2*D
-// bytes of LDS, 128 KiB per workgroup at either head dimension.
-template <int D>
-constexpr int kv_waves() {
-  static_assert(D == 64 || D == 128, "head dim");
-  return D == 128 ? 4 : 8;
-}
-
 template <typename T, int D, bool CAUSAL>
-__global__ void __launch_bounds__(kv_waves<D>() * 64, 1) kvcache_fwd_kernel(KvParams p) {
+__global__ void __launch_bounds__(kv_waves(D) * 64, 1) kvcache_fwd_kernel(KvParams p) {
   using H = Half<T>;
   using Frag = typename H::Frag;
   using Pair = typename H::Pair;
   using Sw = Swizzle<D>;
-  constexpr int NW = kv_waves<D>();
+  constexpr int NW = kv_waves(D);
   constexpr int NT = NW * 64;
   constexpr int RB = D * 2;              // bytes per row of K or V
   constexpr int CPR = D / 8;             // 16-byte chunks per row
@@ -79,9 +71,11 @@ __global__ void __launch_bounds__(kv_waves<D>() * 64, 1) kvcache_fwd_kernel(KvPa
   constexpr int RPL = 1024 / RB;         // rows one 1 KiB load covers
   constexpr int NKS = D / 16;            // MFMAs per score block
   constexpr int ND = D / 32;             // 32-row blocks of O^T
-  constexpr int WAVE_LDS = 2 * 2 * TILE; // [buffer][K, V][tile]
+  constexpr int NBUF = kv_bufs(D);       // LDS stages per wave
+  constexpr int WAVE_LDS = NBUF * 2 * TILE;  // [stage][K, V][tile]
   constexpr int OS = D + 4;              // row stride (floats) of a wave's partial O
   static_assert(NW * kKvRows * OS * 4 <= NW * WAVE_LDS, "merge area fits the tile buffers");
+  static_assert(NBUF >= 2 && NBUF <= 4, "stages");
 
   __shared__ __attribute__((aligned(1024))) char smem[NW * WAVE_LDS];
   __shared__ float m_lds[NW][kKvRows];
@@ -127,24 +121,25 @@ __global__ void __launch_bounds__(kv_waves<D>() * 64, 1) kvcache_fwd_kernel(KvPa
   }
   char* wlds = smem + wave * WAVE_LDS;
   const uint32_t wlds_addr = lds_addr(wlds);
-  auto issue = [&](int i) {  // tile first + i*NW into buffer i & 1
+  auto issue = [&](int i) {  // tile first + i*NW into stage i % NBUF
     const int64_t k0 = (int64_t)(first + i * NW) * kKvKeys;
     const uint32_t rows = (uint32_t)(Nk - k0 < kKvKeys ? Nk - k0 : kKvKeys);
     const u32x4 rk = buffer_rsrc(Kh + k0 * D, rows * RB);
     const u32x4 rv = buffer_rsrc(Vh + k0 * D, rows * RB);
-    const uint32_t base = wlds_addr + (i & 1) * 2 * TILE;
+    const uint32_t base = wlds_addr + (i % NBUF) * 2 * TILE;
 #pragma unroll
     for (int j = 0; j < LPT; ++j) dma_load16(rk, base + j * 1024, kvoff[j]);
 #pragma unroll
     for (int j = 0; j < LPT; ++j) dma_load16(rv, base + TILE + j * 1024, vvoff[j]);
   };
-  // vmcnt(n) with the other counters left alone (gfx9 s_waitcnt encoding);
-  // no LDS read may move above the wait.
-  constexpr int kWaitNext = 0x0F70 | ((2 * LPT) & 15) | (((2 * LPT) >> 4) << 14);
-  constexpr int kWaitAll = 0x0F70;
-  auto wait_vm = [](auto imm) {
+  // Wait until at most `tiles` tiles' loads of this wave are outstanding:
+  // vmcnt(tiles * 2 * LPT) with the other counters left alone (gfx9
+  // s_waitcnt encoding); no LDS read may move above the wait.
+  auto wait_tiles = [](auto tiles) {
+    constexpr int n = decltype(tiles)::value * 2 * LPT;
+    static_assert(n < 64, "vmcnt range");
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(decltype(imm)::value);
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
     asm volatile("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -161,10 +156,12 @@ __global__ void __launch_bounds__(kv_waves<D>() * 64, 1) kvcache_fwd_kernel(KvPa
       qf[ks] = bits<Frag>(raw);
     }
   }
-  if (n_my > 0) issue(0);
+#pragma unroll
+  for (int j = 0; j < NBUF - 1; ++j)
+    if (j < n_my) issue(j);
   // The Q loads must land now: the compiler does not count the tile loads,
   // so a wait it placed for Q inside the loop would also drain the prefetch.
-  wait_vm(std::integral_constant<int, kWaitAll>{});
+  wait_tiles(std::integral_constant<int, 0>{});
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) fence(qf[ks]);
 
@@ -194,13 +191,18 @@ __global__ void __launch_bounds__(kv_waves<D>() * 64, 1) kvcache_fwd_kernel(KvPa
   const int64_t row_end = CAUSAL ? (qrow + 1 + p.off < Nk ? qrow + 1 + p.off : Nk) : Nk;
 
   for (int i = 0; i < n_my; ++i) {
-    if (i + 1 < n_my) {
-      issue(i + 1);
-      wait_vm(std::integral_constant<int, kWaitNext>{});  // tile i has landed
+    // Keep NBUF - 1 tiles in flight; then tile i is the oldest outstanding.
+    if (i + NBUF - 1 < n_my) {
+      issue(i + NBUF - 1);
+      wait_tiles(std::integral_constant<int, NBUF - 1>{});
+    } else if (NBUF >= 3 && n_my - 1 - i == 1) {
+      wait_tiles(std::integral_constant<int, 1>{});
+    } else if (NBUF >= 4 && n_my - 1 - i == 2) {
+      wait_tiles(std::integral_constant<int, (NBUF >= 4 ? 2 : 0)>{});
     } else {
-      wait_vm(std::integral_constant<int, kWaitAll>{});
+      wait_tiles(std::integral_constant<int, 0>{});
     }
-    const char* kl = wlds + (i & 1) * 2 * TILE;
+    const char* kl = wlds + (i % NBUF) * 2 * TILE;
     const char* vl = kl + TILE;
     const int64_t k0 = (int64_t)(first + i * NW) * kKvKeys;
 
@@ -323,38 +325,71 @@ __global__ void __launch_bounds__(kv_waves<D>() * 64, 1) kvcache_fwd_kernel(KvPa
   }
 }
 
-// Merge of the splits' partial results, one thread per 4 output columns of a
-// row: LSE = M + ln sum_s exp(lse_s - M), O = sum_s exp(lse_s - M) O_s / that
-// sum, with M the largest lse_s (the online-softmax rescale rule).
+// Merge of the splits' partial results: LSE = M + ln sum_s exp(lse_s - M),
+// O = sum_s exp(lse_s - M) O_s / that sum, with M the largest lse_s (the
+// online-softmax rescale rule).  One workgroup per output row: thread (g, c)
+// owns output columns 4c..4c+3 and the splits s = g (mod G), so a row's
+// splits are read in parallel; the G partial sums are added through LDS.
 template <typename T, int D>
 __global__ void __launch_bounds__(256) kvcache_merge_kernel(KvParams p) {
   using H = Half<T>;
   using Pair = typename H::Pair;
-  constexpr int TPR = D / 4;  // threads per row
-  const int64_t row = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
-  const int c4 = threadIdx.x % TPR;
-  if (row >= p.rows_total) return;
+  constexpr int TPR = D / 4;     // threads per output row slice
+  constexpr int G = 256 / TPR;   // split groups
+  __shared__ float red[256];
+  __shared__ float4 part[G][TPR];
+  __shared__ float part_l[G];
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int c4 = tid % TPR, g = tid / TPR;
   const int S = p.n_split;
-  float M = kNegInf;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, p.ws_lse[(int64_t)s * p.rows_total + row]);
+  const float* lse_s = p.ws_lse + row;
+  const int64_t stride = p.rows_total;
+
+  float mx = kNegInf;
+  for (int s = tid; s < S; s += 256) mx = fmaxf(mx, lse_s[s * stride]);
+  red[tid] = mx;
+  __syncthreads();
+#pragma unroll
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
+    __syncthreads();
+  }
+  const float M = red[0];
   const float M_use = M == kNegInf ? 0.f : M;
+
   float L = 0.f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = 0; s < S; ++s) {
-    const float wt =
-        __builtin_amdgcn_exp2f((p.ws_lse[(int64_t)s * p.rows_total + row] - M_use) * kLog2e);
+  for (int s = g; s < S; s += G) {
+    const float wt = __builtin_amdgcn_exp2f((lse_s[s * stride] - M_use) * kLog2e);
+    const float4 x = *(const float4*)(p.ws_o + ((int64_t)s * stride + row) * D + 4 * c4);
     L += wt;
-    const float4 x = *(const float4*)(p.ws_o + ((int64_t)s * p.rows_total + row) * D + 4 * c4);
     acc.x += wt * x.x;
     acc.y += wt * x.y;
     acc.z += wt * x.z;
     acc.w += wt * x.w;
   }
-  const float inv = 1.0f / L;
-  const Pair a = H::pack(acc.x * inv, acc.y * inv);
-  const Pair b = H::pack(acc.z * inv, acc.w * inv);
-  *(u32x2*)((T*)p.o + row * D + 4 * c4) = u32x2{bits<uint32_t>(a), bits<uint32_t>(b)};
-  if (c4 == 0) p.lse[row] = M + __builtin_amdgcn_logf(L) * kLn2;
+  part[g][c4] = acc;
+  if (c4 == 0) part_l[g] = L;
+  __syncthreads();
+  if (g == 0) {
+    L = 0.f;
+    acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const float4 x = part[j][c4];
+      L += part_l[j];
+      acc.x += x.x;
+      acc.y += x.y;
+      acc.z += x.z;
+      acc.w += x.w;
+    }
+    const float inv = 1.0f / L;
+    const Pair a = H::pack(acc.x * inv, acc.y * inv);
+    const Pair b = H::pack(acc.z * inv, acc.w * inv);
+    *(u32x2*)((T*)p.o + row * D + 4 * c4) = u32x2{bits<uint32_t>(a), bits<uint32_t>(b)};
+    if (c4 == 0) p.lse[row] = M + __builtin_amdgcn_logf(L) * kLn2;
+  }
 }
 
 template <typename T, int D, bool CAUSAL>
@@ -377,13 +412,12 @@ hipError_t launch(const KvArgs& a, hipStream_t stream) {
   p.c = __builtin_fmaxf(__builtin_fabsf(a.scale) * kLog2e, 1.17549435e-38f);
   p.q_sign = a.scale < 0.f ? 0x80008000u : 0u;
   const unsigned grid = (unsigned)(a.BH * p.n_qblk * p.n_split);
-  hipLaunchKernelGGL((kvcache_fwd_kernel<T, D, CAUSAL>), dim3(grid), dim3(kv_waves<D>() * 64), 0,
+  hipLaunchKernelGGL((kvcache_fwd_kernel<T, D, CAUSAL>), dim3(grid), dim3(kv_waves(D) * 64), 0,
                      stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
-  constexpr int RPB = 256 / (D / 4);
-  hipLaunchKernelGGL((kvcache_merge_kernel<T, D>), dim3((unsigned)((p.rows_total + RPB - 1) / RPB)),
-                     dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((kvcache_merge_kernel<T, D>), dim3((unsigned)p.rows_total), dim3(256), 0,
+                     stream, p);
   return hipGetLastError();
 }
 

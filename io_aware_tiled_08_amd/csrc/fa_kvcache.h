@@ -32,8 +32,11 @@ struct KvArgs {
   int tiles_per_split;  // 32-key tiles per range
 };
 
-// Waves per workgroup of the cache kernel at head dimension d.
-inline int kv_waves(int d) { return d == 128 ? 4 : 8; }
+// Waves per workgroup and LDS stages per wave of the cache kernel at head
+// dimension d.  A stage is one 32-key K tile and one V tile (128*d bytes); a
+// wave keeps kv_bufs - 1 tiles in flight while it computes on another.
+constexpr int kv_waves(int d) { return d == 128 ? 4 : 8; }
+constexpr int kv_bufs(int d) { return d == 128 ? 2 : 2; }
 
 // Enqueue the cache kernel (and, with n_split > 1, the merge kernel).
 hipError_t launch_kvcache(const KvArgs& a, hipStream_t stream);  // FA_F16, FA_BF16

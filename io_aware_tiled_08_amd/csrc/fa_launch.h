@@ -32,6 +32,12 @@ inline int rows_per_workgroup(Dtype dtype) {
   return dtype == Dtype::F32 ? kRowsPerWorkgroupF32 : kRowsPerWorkgroupF16;
 }
 
+// Threads per workgroup of the forward kernel (the dispatch's total thread
+// count, workgroups x this, must fit 32 bits).
+inline int threads_per_workgroup(Dtype dtype, int d) {
+  return dtype == Dtype::F32 ? (d == 64 ? 8 : 4) * 64 : 512;
+}
+
 // Enqueue the forward kernel on `stream`; arguments are already validated.
 hipError_t launch_forward_f16(const FwdArgs& a, hipStream_t stream);  // FA_F16, FA_BF16
 hipError_t launch_forward_f32(const FwdArgs& a, hipStream_t stream);

@@ -264,3 +264,13 @@ def test_kv_no_device_reported_not_crashed(L):
         pytest.skip("a GPU is present")
     st, msg = _kv(L, splits=4)
     assert st == 8, msg
+
+
+def test_dispatch_thread_count_limit(L):
+    # 2^20 heads x 8 blocks of 256 rows x 512 threads overflows the 32-bit
+    # dispatch size although the workgroup count fits 31 bits.
+    assert _call(L, B=1 << 20, H=1, N=2048)[0] == 2
+    assert _call(L, B=1 << 20, H=1, N=1792)[0] != 2
+    # cache path: 2^23 rows need 2^31 merge threads
+    st, _ = _kv(L, B=1 << 23, H=1, Nq=1, Nk=4096, splits=2, ws_bytes=1 << 62)
+    assert st == 2
