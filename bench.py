@@ -59,10 +59,15 @@ COPY_REPS = 3
 
 
 def kernel_source_digest(key: str) -> str:
+    """sha256 of the kernel's sources with comments and blank space removed,
+    so that only a change to the code itself invalidates stored counters."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[key]:
-        with open(os.path.join(_CSRC, name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(_CSRC, name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 

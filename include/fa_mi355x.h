@@ -106,9 +106,10 @@ fa_status flash_attn_fwd(const void* q, const void* k, const void* v,
  * flash_attn_fwd_kvcache -- attention of Nq new queries against a key/value
  * cache of Nk rows (decode), fp16 or bf16.
  *
- * Source: "KV Cache: Why Generation Speeds Up" (generation stores and reuses
- * the keys and values of earlier tokens) for the operation; the computation is
- * the one of flash_attn_fwd (same pages).  Reading where the pages are silent:
+ * Source: "FlashAttention: Tiled & Fused", related-diagram card "KV Cache: Why
+ * Generation Speeds Up" (generation stores and reuses the keys and values of
+ * earlier tokens) for the operation; the computation is the one of
+ * flash_attn_fwd (same pages).  Reading where the pages are silent:
  * the Nq queries are the last Nq positions of the sequence whose Nk keys are
  * cached, so with causal != 0 query i sees the keys j <= i + (Nk - Nq); with
  * Nq == Nk that is flash_attn_fwd's mask.

@@ -3,8 +3,9 @@
 //
 // What is computed: for every (batch, head), the Nq query rows are the last Nq
 // positions of a sequence whose keys and values are all in the cache (Nk rows;
-// "KV Cache: Why Generation Speeds Up": generation stores and reuses the keys
-// and values of earlier tokens).  O = softmax(scale * Q K^T) V and the
+// "FlashAttention: Tiled & Fused", related-diagram card "KV Cache: Why
+// Generation Speeds Up": generation stores and reuses the keys and values of
+// earlier tokens).  O = softmax(scale * Q K^T) V and the
 // natural-log LSE of each score row, where a causal query i sees the keys
 // j <= i + (Nk - Nq).  The method is the one of the square kernel: K and V
 // tiles staged on chip, an online softmax with a running maximum and sum

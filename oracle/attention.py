@@ -45,8 +45,10 @@ it):
 * causal means query i sees key j iff j <= i (square, diagonal included); the
   pages never treat masking;
 * K and V may be longer than Q (Nk >= Nq rows): the key/value cache of the
-  "KV Cache: Why Generation Speeds Up" card (past keys and values are kept;
-  each new token computes only its own).  The Nq queries are then the last Nq
+  "KV Cache: Why Generation Speeds Up" card among the related diagrams of
+  "FlashAttention: Tiled & Fused" (in generation the keys and values
+  of earlier tokens are stored and reused; only the newest token's are
+  computed).  The Nq queries are then the last Nq
   positions of the sequence, so a causal query i sees key j iff
   j <= i + (Nk - Nq); with Nq = Nk this is the square rule above;
 * LSE is the natural-log log-sum-exp of the scaled, masked scores of a row;
