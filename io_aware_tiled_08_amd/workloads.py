@@ -263,3 +263,38 @@ def sample_rows(seed: int, B: int, H: int, N: int, count: int) -> np.ndarray:
 def workload_inputs(w: Workload):
     """(q, k, v) CPU tensors for a named workload."""
     return random_qkv(w.B, w.H, w.N, w.d, w.dtype, w.seed, w.kind)
+
+
+E4M3_MAX = 448.0  # largest finite e4m3 value
+
+
+def quantize_e4m3(x32: np.ndarray):
+    """Per-tensor scaled e4m3 quantization: descale = float32(amax / 448),
+    codes = round-to-nearest-even of x / descale (float32 division), as a
+    torch float8_e4m3fn tensor.  Returns (codes, descale)."""
+    t = torch.from_numpy(np.ascontiguousarray(x32, dtype=np.float32))
+    amax = float(t.abs().max()) if t.numel() else 0.0
+    descale = float(np.float32(amax / E4M3_MAX)) if amax > 0 else 1.0
+    codes = (t / np.float32(descale)).to(torch.float8_e4m3fn)
+    return codes, descale
+
+
+def random_qkv_fp8(B: int, H: int, N: int, d: int, seed: int, Nk: Optional[int] = None):
+    """Q [B, H, N, d] and K, V [B, H, Nk, d] as e4m3 tensors with per-tensor
+    descale factors: the float32 N(0,1) draws of random_qkv (same seeds and
+    tensor ids, one head slice at a time), each tensor quantized with
+    quantize_e4m3.  Returns (q, k, v, q_descale, k_descale, v_descale)."""
+    Nk = N if Nk is None else Nk
+
+    def draw(tensor_id, n):
+        rng = np.random.default_rng([seed, tensor_id])
+        out = np.empty((B, H, n, d), dtype=np.float32)
+        for b in range(B):
+            for h in range(H):
+                out[b, h] = rng.standard_normal((n, d), dtype=np.float32)
+        return out
+
+    q, qs = quantize_e4m3(draw(TENSOR_Q, N))
+    k, ks = quantize_e4m3(draw(TENSOR_K, Nk))
+    v, vs = quantize_e4m3(draw(TENSOR_V, Nk))
+    return q, k, v, qs, ks, vs

@@ -263,3 +263,78 @@ def streaming_attention(q, k, v, scale: float, causal: bool = False,
                 O[b, h, r] = acc / l
                 LSE[b, h, r] = m + math.log(l)
     return O, LSE
+
+
+def decode_e4m3(codes) -> np.ndarray:
+    """float64 value of each e4m3 code (uint8 array): sign bit 7, exponent bits
+    6..3 with bias 7, mantissa bits 2..0; exponent 0 is subnormal
+    (m * 2^-9); exponent 15 with mantissa 7 is NaN; no infinities."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = (c & 7).astype(np.float64)
+    val = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    val = np.where((e == 15) & ((c & 7) == 7), np.nan, val)
+    return sign * val
+
+
+def dequantize_fp8(x, descale: float) -> np.ndarray:
+    """Exact float64 value of an e4m3 tensor (torch float8_e4m3fn or a uint8
+    code array) times float64(float32(descale))."""
+    if hasattr(x, "detach"):
+        import torch
+        x = x.detach().cpu()
+        if x.dtype != torch.uint8:
+            x = x.view(torch.uint8)
+        x = x.numpy()
+    return decode_e4m3(x) * float(np.float64(np.float32(descale)))
+
+
+def fp8_weight_error_bound(q, k, v, scale: float, causal: bool = False, rows=None,
+                           u: float = 2.0 ** -4, a: float = 2.0 ** -10
+                           ) -> Tuple[np.ndarray, np.ndarray]:
+    """Bound on |O_hat - O| (per element) and |LSE_hat - LSE| (per row) for a
+    forward pass that computes the scores exactly enough and rounds each
+    softmax weight to e4m3 before the P V product and the row sum.
+
+    Derivation.  The pass weights key j by w_j = 2^(c*s_j - m_ref) for a
+    reference m_ref in [m_max - 8, m_max], rounds it to nearest-even e4m3 and
+    uses the rounded weights in both sums.  Rounding to e4m3 moves a weight by
+    at most half a unit in the last place: relative 2^-4 in the normal range,
+    absolute 2^-10 below 2^-6 (subnormals, spacing 2^-9).  So
+    |w_hat_j - w_j| <= e_j = max(u * w_j, a).  With W = sum w_j and
+    E = sum e_j,
+        O_hat - O = sum_j (w_hat_j - w_j)(v_j - O) / sum_j w_hat_j
+        |O_hat - O| <= sum_j e_j |v_j - O| / (W - E)
+        |LSE_hat - LSE| = |ln(sum w_hat / sum w)| <= -ln(1 - E / W).
+    The relative part scales with the weights and the absolute part does not,
+    so the bound is largest for the smallest scale, m_ref = m_max, where the
+    weights are exp(S_j - S_max) <= 1; that is the scale used here.
+    Inputs are exact values (float64, already dequantized).
+    """
+    Q, K, V = as_f64(q), as_f64(k), as_f64(v)
+    B, H, Nq, Nk, d = _shapes(Q, K, V)
+    off = causal_offset(Nq, Nk) if causal else 0
+    s64 = boundary_scale(scale)
+    idx_all = _row_index(rows, B, H, Nq)
+    R = idx_all.shape[-1]
+    bO = np.zeros((B, H, R, d))
+    bL = np.zeros((B, H, R))
+    for b in range(B):
+        for h in range(H):
+            for r0 in range(0, R, 128):
+                idx = np.asarray(idx_all[b, h, r0:r0 + 128])
+                top = min(Nk, int(idx.max()) + 1 + off) if causal else Nk
+                S = (Q[b, h, idx] @ K[b, h, :top].T) * s64
+                if causal:
+                    S[np.arange(top)[None, :] > idx[:, None] + off] = -np.inf
+                w = np.exp(S - S.max(axis=1, keepdims=True))
+                e = np.where(np.isfinite(S), np.maximum(u * w, a), 0.0)
+                W = w.sum(axis=1)
+                E = e.sum(axis=1)
+                O = (w @ V[b, h, :top]) / W[:, None]
+                # sum_j e_j |v_jc - O_c| for every column c
+                dev = np.abs(V[b, h, :top][None, :, :] - O[:, None, :])
+                bO[b, h, r0:r0 + len(idx)] = np.einsum("rj,rjc->rc", e, dev) / (W - E)[:, None]
+                bL[b, h, r0:r0 + len(idx)] = -np.log1p(-E / W)
+    return bO, bL
