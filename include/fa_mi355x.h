@@ -28,7 +28,7 @@
 extern "C" {
 #endif
 
-#define FA_MI355X_ABI_VERSION 2
+#define FA_MI355X_ABI_VERSION 3
 
 typedef enum {
   FA_F32 = 0,   /* IEEE binary32 */
@@ -154,6 +154,38 @@ fa_status flash_attn_fwd_kvcache(const void* q, const void* k, const void* v,
                                  int num_splits, void* workspace,
                                  int64_t workspace_bytes,
                                  fa_dtype dtype, void* stream);
+
+/*
+ * flash_attn_fwd_fp8 -- the forward pass of flash_attn_fwd on 8-bit inputs.
+ *
+ * Source: "FlashAttention" (Chapter 15, vizuara), "FlashAttention Evolution"
+ * (the later versions add FP8 support); the computation is flash_attn_fwd's.
+ * Inputs are e4m3 codes (OCP "fn" variant: 1 sign, 4 exponent bits with bias
+ * 7, 3 mantissa bits, no infinities, 0x7F/0xFF NaN) with one descale factor
+ * per tensor: the value of element x of q is code(x) * q_descale, likewise for
+ * k and v.  For each b, h and query row i < N:
+ *   s_ij   = scale * sum_c qval[b,h,i,c] * kval[b,h,j,c]   for visible keys j
+ *   o[b,h,i,:] = sum_j softmax_j(s_ij) * vval[b,h,j,:]      (bfloat16)
+ *   lse[b,h,i] = ln(sum_j exp(s_ij))                          (float32)
+ * with flash_attn_fwd's causal mask.  Both products run on the 8-bit matrix
+ * unit; the softmax weights are rounded to e4m3 before the second product,
+ * and the row sum adds the rounded weights.  Accuracy contract: per element,
+ * |o - exact| <= sum_j max(w_j/16, 2^-10) |v_j - o_exact| / (sum_j w_j - sum_j
+ * max(w_j/16, 2^-10)) (w_j = exp(s_ij - max_j s_ij)) plus the bfloat16
+ * rounding of o; per row, |lse - exact| <= -ln(1 - that sum of terms / sum w).
+ *
+ * Arguments: q, k, v device pointers to contiguous [B, H, N, d] byte arrays;
+ * o a contiguous [B, H, N, d] bfloat16 array; lse [B, H, N] float32; B, H,
+ * N, d, scale, causal and stream as for flash_attn_fwd; q_descale,
+ * k_descale, v_descale finite and > 0 (else FA_ERR_SCALE).  Same ownership,
+ * alignment, overlap rules, synchronisation and errors as flash_attn_fwd.
+ */
+fa_status flash_attn_fwd_fp8(const void* q, const void* k, const void* v,
+                             void* o, float* lse,
+                             int64_t B, int64_t H, int64_t N, int64_t d,
+                             float scale, int causal,
+                             float q_descale, float k_descale, float v_descale,
+                             void* stream);
 
 /* Key ranges flash_attn_fwd_kvcache uses for these sizes and num_splits (1
  * for empty or invalid sizes).  No HIP call. */

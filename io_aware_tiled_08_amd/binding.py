@@ -23,10 +23,10 @@ STATUS = {
     8: "FA_ERR_NO_DEVICE", 9: "FA_ERR_ARCH", 10: "FA_ERR_HIP", 11: "FA_ERR_WORKSPACE",
 }
 STATUS_CODE = {name: code for code, name in STATUS.items()}
-EXPORTS = ("flash_attn_fwd", "flash_attn_fwd_kvcache", "flash_attn_kvcache_splits",
+EXPORTS = ("flash_attn_fwd", "flash_attn_fwd_fp8", "flash_attn_fwd_kvcache", "flash_attn_kvcache_splits",
            "flash_attn_kvcache_workspace_size", "flash_attn_status_str",
            "flash_attn_last_error", "flash_attn_abi_version")
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _lib = None
 _lock = threading.Lock()
@@ -57,6 +57,10 @@ def lib() -> ctypes.CDLL:
             L.flash_attn_fwd.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 4 + [
                 ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
             L.flash_attn_fwd.restype = ctypes.c_int
+            L.flash_attn_fwd_fp8.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 4 + [
+                ctypes.c_float, ctypes.c_int, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                ctypes.c_void_p]
+            L.flash_attn_fwd_fp8.restype = ctypes.c_int
             L.flash_attn_fwd_kvcache.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 5 + [
                 ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
                 ctypes.c_int, ctypes.c_void_p]
@@ -223,6 +227,51 @@ def flash_attn_fwd_kvcache(q, k, v, o=None, lse=None, *, scale: Optional[float] 
                                       lse.data_ptr(), B, H, Nq, Nk, d, float(scale),
                                       int(bool(causal)), int(num_splits), ws_ptr, ws_bytes,
                                       code, s.cuda_stream)
+    if st != 0:
+        raise FlashAttnError(st, L.flash_attn_last_error().decode())
+    return o, lse
+
+
+def flash_attn_fwd_fp8(q, k, v, o=None, lse=None, *, q_descale: float, k_descale: float,
+                       v_descale: float, scale: Optional[float] = None, causal: bool = False,
+                       stream=None) -> Tuple["object", "object"]:
+    """8-bit forward: q, k, v contiguous [B, H, N, d] torch.float8_e4m3fn device
+    tensors whose values are code * descale (one factor per tensor).  Returns
+    O as bfloat16 [B, H, N, d] and LSE as float32 [B, H, N]; o and lse may be
+    preallocated.  scale defaults to 1/sqrt(d).  Enqueued on `stream` (default:
+    the current stream of q's device) without synchronising."""
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise ValueError(f"{name} must be a device tensor")
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [B, H, N, d] tensor")
+        if t.dtype != torch.float8_e4m3fn:
+            raise TypeError(f"{name} must be torch.float8_e4m3fn (got {t.dtype})")
+    if k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("q, k and v must have the same shape")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError("q, k and v must be on the same device")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if (o.shape != q.shape or o.dtype != torch.bfloat16 or o.device != q.device
+            or not o.is_contiguous()):
+        raise ValueError("o must be a contiguous bfloat16 tensor of q's shape")
+    if (lse.shape != (B, H, N) or lse.dtype != torch.float32 or lse.device != q.device
+            or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    L = lib()
+    with torch.cuda.device(q.device):
+        s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        st = L.flash_attn_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                  lse.data_ptr(), B, H, N, d, float(scale), int(bool(causal)),
+                                  float(q_descale), float(k_descale), float(v_descale),
+                                  s.cuda_stream)
     if st != 0:
         raise FlashAttnError(st, L.flash_attn_last_error().decode())
     return o, lse

@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <cstring>
 
+#include "fa_fp8.h"
 #include "fa_kvcache.h"
 #include "fa_launch.h"
 
@@ -159,6 +160,62 @@ fa_status flash_attn_fwd(const void* q, const void* k, const void* v, void* o, f
   (void)hipGetLastError();  // do not report an earlier, unrelated error
   const hipError_t e = dtype == FA_F32 ? fa::launch_forward_f32(a, (hipStream_t)stream)
                                        : fa::launch_forward_f16(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
+fa_status flash_attn_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
+                             int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
+                             float q_descale, float k_descale, float v_descale, void* stream) {
+  g_last_error[0] = '\0';
+  if (B < 0 || H < 0 || N < 0)
+    return fail(FA_ERR_SHAPE, "B, H, N must be >= 0 (got %lld, %lld, %lld)", (long long)B,
+                (long long)H, (long long)N);
+  if (d != 64 && d != 128) return fail(FA_ERR_HEAD_DIM, "d must be 64 or 128 (got %lld)", (long long)d);
+  if (!std::isfinite(scale)) return fail(FA_ERR_SCALE, "scale must be finite");
+  if (!(std::isfinite(q_descale) && q_descale > 0.f && std::isfinite(k_descale) &&
+        k_descale > 0.f && std::isfinite(v_descale) && v_descale > 0.f))
+    return fail(FA_ERR_SCALE, "descale factors must be finite and > 0");
+  if (B == 0 || H == 0 || N == 0) return FA_OK;
+  if (!q || !k || !v || !o || !lse) return fail(FA_ERR_NULL, "q, k, v, o and lse must be non-NULL");
+  const uintptr_t mis = ((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)lse) & 15u;
+  if (mis) return fail(FA_ERR_ALIGN, "q, k, v, o and lse must be 16-byte aligned");
+  const int64_t kLimit = (int64_t)1 << 62;
+  if (B > kLimit / H || N > kLimit / (B * H) || d * 2 > kLimit / (B * H * N))
+    return fail(FA_ERR_SHAPE, "B*H*N*d*elem overflows");
+  const int64_t BH = B * H;
+  const int64_t n_qblk = (N + fa::kRowsPerWorkgroupFp8 - 1) / fa::kRowsPerWorkgroupFp8;
+  if (n_qblk > INT32_MAX || BH * n_qblk > (int64_t)UINT32_MAX / 512)
+    return fail(FA_ERR_SHAPE, "B*H*ceil(N/%d) = %lld workgroups exceeds the grid limit",
+                fa::kRowsPerWorkgroupFp8, (long long)(BH * n_qblk));
+  const int64_t ibytes = BH * N * d;      // e4m3 inputs
+  const int64_t obytes = BH * N * d * 2;  // bf16 output
+  const int64_t lbytes = BH * N * 4;
+  if (overlaps(o, obytes, q, ibytes) || overlaps(o, obytes, k, ibytes) ||
+      overlaps(o, obytes, v, ibytes) || overlaps(lse, lbytes, q, ibytes) ||
+      overlaps(lse, lbytes, k, ibytes) || overlaps(lse, lbytes, v, ibytes) ||
+      overlaps(lse, lbytes, o, obytes))
+    return fail(FA_ERR_ALIAS, "o and lse must not overlap q, k, v or each other");
+
+  fa_status st = check_device();
+  if (st != FA_OK) return st;
+
+  fa::Fp8Args a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.BH = BH;
+  a.N = N;
+  a.d = (int)d;
+  a.scale = scale;
+  a.causal = causal != 0;
+  a.q_descale = q_descale;
+  a.k_descale = k_descale;
+  a.v_descale = v_descale;
+  (void)hipGetLastError();
+  const hipError_t e = fa::launch_forward_fp8(a, (hipStream_t)stream);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return FA_OK;
 }
