@@ -37,7 +37,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 # MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s).
-MFMA_PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3}
+MFMA_PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "f32": 157.3, "fp8_e4m3": 5033.2}
 HBM_PEAK_GBPS = 8000.0
 PEAK_CLOCK_MHZ = 2400.0  # the engine clock the published MFMA peaks are quoted at
 _CSRC = os.path.join(ROOT, "io_aware_tiled_08_amd", "csrc")
@@ -47,12 +47,14 @@ KERNEL_SOURCES = {
     "bf16": ("fa_fwd_f16.hip", "fa_f16_common.h", "fa_device.h"),
     "f32": ("fa_fwd_f32.hip", "fa_device.h"),
     "kvcache": ("fa_fwd_kvcache.hip", "fa_f16_common.h", "fa_device.h"),
+    "fp8": ("fa_fwd_fp8.hip", "fa_f16_common.h", "fa_device.h"),
 }
 # (dominant kernel, every kernel of one call) name patterns in rocprofv3 output
 KERNEL_NAME_PATTERN = {"f16": ("fwd_f16_kernel", "fwd_f16_kernel"),
                        "bf16": ("fwd_f16_kernel", "fwd_f16_kernel"),
                        "f32": ("fwd_f32_kernel", "fwd_f32_kernel"),
-                       "kvcache": ("kvcache_fwd_kernel", "kvcache_")}
+                       "kvcache": ("kvcache_fwd_kernel", "kvcache_"),
+                       "fp8": ("fwd_fp8_kernel", "fwd_fp8_kernel")}
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 512 << 20  # one calibration copy: 512 MiB read + 512 MiB written
 COPY_REPS = 3
@@ -79,8 +81,10 @@ def workload_by_name(name: str):
         return w, w.dtype
     if name in W.CACHE_WORKLOADS:
         return W.CACHE_WORKLOADS[name], "kvcache"
+    if name in W.FP8_WORKLOADS:
+        return W.FP8_WORKLOADS[name], "fp8"
     raise SystemExit(f"unknown workload {name!r}; known: "
-                     f"{sorted(W.WORKLOADS) + sorted(W.CACHE_WORKLOADS)}")
+                     f"{sorted(W.WORKLOADS) + sorted(W.CACHE_WORKLOADS) + sorted(W.FP8_WORKLOADS)}")
 
 
 def traffic_path(workload: str) -> str:
@@ -387,6 +391,16 @@ def main():
         def step():
             flash_attn_fwd_kvcache(qd, kd, vd, o, lse, scale=w.scale, causal=w.causal,
                                    workspace=ws, stream=stream)
+    elif key == "fp8":
+        from io_aware_tiled_08_amd import flash_attn_fwd_fp8
+        q, k, v, qs, ks, vs = W.fp8_workload_inputs(w)
+        qd, kd, vd = (x.to(dev) for x in (q, k, v))
+        o = torch.empty(tuple(q.shape), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+
+        def step():
+            flash_attn_fwd_fp8(qd, kd, vd, o, lse, q_descale=qs, k_descale=ks, v_descale=vs,
+                               scale=w.scale, causal=w.causal, stream=stream)
     else:
         q, k, v = W.workload_inputs(w)
         qd, kd, vd = (x.to(dev) for x in (q, k, v))
@@ -510,7 +524,8 @@ def main():
             roofline["gfx_clock_mhz_median"] = round(mhz, 1)
             roofline["frac_at_measured_clock"] = round(tflops / (peak * mhz / PEAK_CLOCK_MHZ), 4)
         result = {
-            "metric": "attention fwd TFLOP/s and % of MFMA peak, N=4096 d=128 fp16 (1 GPU)",
+            "metric": ("attention fwd TFLOP/s and % of MFMA peak, e4m3 inputs (1 GPU)" if key == "fp8"
+                       else "attention fwd TFLOP/s and % of MFMA peak, N=4096 d=128 fp16 (1 GPU)"),
             "value": round(tflops, 2),
             "unit": "TFLOP/s",
             "n_gpus": 1,
@@ -530,8 +545,14 @@ def main():
                         "arch": getattr(props, "gcnArchName", "")}
     result["timed_wall_s"] = round(wall, 4)
     if args.cpu_budget > 0:
-        result["cpu_baseline"] = (cpu_baseline_cache(w, q, k, v, args.cpu_budget) if cache
-                                  else cpu_baseline(w, q, k, v, args.cpu_budget))
+        if cache:
+            result["cpu_baseline"] = cpu_baseline_cache(w, q, k, v, args.cpu_budget)
+        elif key == "fp8":
+            import oracle
+            qx, kx, vx = (oracle.dequantize_fp8(x, s) for x, s in ((q, qs), (k, ks), (v, vs)))
+            result["cpu_baseline"] = cpu_baseline(w, qx, kx, vx, args.cpu_budget)
+        else:
+            result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

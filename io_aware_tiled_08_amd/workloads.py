@@ -298,3 +298,44 @@ def random_qkv_fp8(B: int, H: int, N: int, d: int, seed: int, Nk: Optional[int] 
     k, ks = quantize_e4m3(draw(TENSOR_K, Nk))
     v, vs = quantize_e4m3(draw(TENSOR_V, Nk))
     return q, k, v, qs, ks, vs
+
+
+@dataclasses.dataclass(frozen=True)
+class Fp8Workload:
+    """The 8-bit forward pass: e4m3 Q, K, V ([B, H, N, d], per-tensor
+    descales), bf16 O."""
+
+    name: str
+    seed: int
+    B: int
+    H: int
+    N: int
+    d: int
+    causal: bool
+    dtype: str = "fp8_e4m3"
+    description: str = ""
+
+    @property
+    def scale(self) -> float:
+        return default_scale(self.d)
+
+    def flops(self) -> float:
+        return metric_flops(self.B, self.H, self.N, self.d, self.causal)
+
+    def compulsory_bytes(self) -> int:
+        """Read 1-byte Q, K, V; write 2-byte O and 4-byte LSE."""
+        n = self.B * self.H * self.N * self.d
+        return 3 * n + 2 * n + 4 * self.B * self.H * self.N
+
+
+# The headline shape with 8-bit inputs (same seed as the fp16 headline draws).
+FP8_WORKLOADS = {
+    "headline_fp8_d128": Fp8Workload(
+        "headline_fp8_d128", 3, 2, 16, 4096, 128, False,
+        description="B=2 H=16 N=4096 d=128, N(0,1) drawn in fp32 and quantized to e4m3 "
+                    "with per-tensor descale amax/448, bf16 O, non-causal"),
+}
+
+
+def fp8_workload_inputs(w: Fp8Workload):
+    return random_qkv_fp8(w.B, w.H, w.N, w.d, w.seed)
