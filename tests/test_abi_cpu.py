@@ -274,3 +274,37 @@ def test_dispatch_thread_count_limit(L):
     # cache path: 2^23 rows need 2^31 merge threads
     st, _ = _kv(L, B=1 << 23, H=1, Nq=1, Nk=4096, splits=2, ws_bytes=1 << 62)
     assert st == 2
+
+
+# ---- flash_attn_fwd_fp8: argument checks before any HIP call -------------
+def _f8(L, q=Q, k=K, v=V, o=O, lse=LSE, B=2, H=3, N=100, d=64, scale=0.125, causal=0,
+        qs=0.01, ks=0.02, vs=0.03):
+    st = L.flash_attn_fwd_fp8(q, k, v, o, lse, B, H, N, d, scale, causal, qs, ks, vs, None)
+    return st, L.flash_attn_last_error().decode()
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "o", "lse"])
+def test_fp8_null_pointer(L, field):
+    assert _f8(L, **{field: None})[0] == 1
+
+
+@pytest.mark.parametrize("bad", [{"qs": 0.0}, {"ks": -1.0}, {"vs": math.inf}, {"qs": math.nan},
+                                 {"scale": math.inf}])
+def test_fp8_scale_and_descales(L, bad):
+    assert _f8(L, **bad)[0] == 6
+
+
+def test_fp8_shapes_head_dim_alignment_alias(L):
+    assert _f8(L, B=-1)[0] == 2
+    assert _f8(L, d=96)[0] == 3
+    assert _f8(L, k=K + 4)[0] == 5
+    assert _f8(L, o=V)[0] == 7
+    assert _f8(L, B=0, q=None, o=None) == (0, "")
+    assert _f8(L, B=1 << 20, H=1, N=2048)[0] == 2
+
+
+def test_fp8_no_device_reported_not_crashed(L):
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _f8(L)[0] == 8
