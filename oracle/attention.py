@@ -338,3 +338,78 @@ def fp8_weight_error_bound(q, k, v, scale: float, causal: bool = False, rows=Non
                 bO[b, h, r0:r0 + len(idx)] = np.einsum("rj,rjc->rc", e, dev) / (W - E)[:, None]
                 bL[b, h, r0:r0 + len(idx)] = -np.log1p(-E / W)
     return bO, bL
+
+
+def attention_backward(q, k, v, do, scale: float, causal: bool = False):
+    """(dQ, dK, dV, D) in float64 for upstream gradient dO, where
+    D[i] = sum_c dO[i, c] * O[i, c] with O the exact forward output.
+
+    Per (b, h): S = scale Q K^T (masked), P = softmax_rows(S), O = P V,
+    dV = P^T dO, dP = dO V^T, dS = P * (dP - D), dQ = scale dS K,
+    dK = scale dS^T Q.  Square (Nq = Nk) inputs.
+    """
+    Q, K, V, dO = as_f64(q), as_f64(k), as_f64(v), as_f64(do)
+    if Q.shape != K.shape or V.shape != Q.shape or dO.shape != Q.shape or Q.ndim != 4:
+        raise ValueError("q, k, v, do must share one [B, H, N, d] shape")
+    B, H, N, d = Q.shape
+    s64 = boundary_scale(scale)
+    dQ, dK, dV = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
+    Dm = np.zeros((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            S = Q[b, h] @ K[b, h].T * s64
+            if causal:
+                S[np.triu(np.ones((N, N), dtype=bool), 1)] = -np.inf
+            m = S.max(axis=1, keepdims=True)
+            E = np.exp(S - m)
+            P = E / E.sum(axis=1, keepdims=True)
+            O = P @ V[b, h]
+            Dv = (dO[b, h] * O).sum(axis=1)
+            dP = dO[b, h] @ V[b, h].T
+            dS = P * (dP - Dv[:, None])
+            dV[b, h] = P.T @ dO[b, h]
+            dQ[b, h] = s64 * (dS @ K[b, h])
+            dK[b, h] = s64 * (dS.T @ Q[b, h])
+            Dm[b, h] = Dv
+    return dQ, dK, dV, Dm
+
+
+def backward_error_bound(q, k, v, do, scale: float, causal: bool = False, u: float = 2.0 ** -11,
+                         u_o: Optional[float] = None):
+    """Per-element bounds on |dQ_hat - dQ|, |dK_hat - dK|, |dV_hat - dV| for a
+    backward pass that (1) rounds P to a type with unit roundoff u before
+    dV = P^T dO, (2) forms dS = P (dP - D) in fp32 with D = rowsum(dO * O_in)
+    where O_in is the forward output rounded to unit u_o (default u), and (3)
+    rounds dS to unit u before dQ = scale dS K and dK = scale dS^T Q.  Inputs
+    are exact (already in the 16-bit type); products of 16-bit values and
+    fp32 sums are exact up to fp32 accumulation, which is left to the caller's
+    absolute slack.
+
+    Derivation.  |P_hat - P| <= u P gives |dV_hat - dV|_jc <= u sum_i P_ij |dO_ic|.
+    O_in = O (1 + e), |e| <= u_o, so |D_hat - D|_i <= u_o sum_c |dO_ic O_ic| =: dD_i,
+    and dS_hat = round(P (dP - D_hat)) differs from dS by at most
+    P_ij dD_i + u (|dS_ij| + P_ij dD_i) =: e_ij.  Then
+    |dQ_hat - dQ|_ic <= scale sum_j e_ij |K_jc| and
+    |dK_hat - dK|_jc <= scale sum_i e_ij |Q_ic|.
+    """
+    u_o = u if u_o is None else u_o
+    Q, K, V, dO = as_f64(q), as_f64(k), as_f64(v), as_f64(do)
+    B, H, N, d = Q.shape
+    s64 = abs(boundary_scale(scale))
+    bQ, bK, bV = np.zeros_like(Q), np.zeros_like(K), np.zeros_like(V)
+    for b in range(B):
+        for h in range(H):
+            S = Q[b, h] @ K[b, h].T * boundary_scale(scale)
+            if causal:
+                S[np.triu(np.ones((N, N), dtype=bool), 1)] = -np.inf
+            E = np.exp(S - S.max(axis=1, keepdims=True))
+            P = E / E.sum(axis=1, keepdims=True)
+            O = P @ V[b, h]
+            Dv = (dO[b, h] * O).sum(axis=1)
+            dS = P * (dO[b, h] @ V[b, h].T - Dv[:, None])
+            dD = u_o * np.abs(dO[b, h] * O).sum(axis=1)
+            e = P * dD[:, None] + u * (np.abs(dS) + P * dD[:, None])
+            bV[b, h] = u * (P.T @ np.abs(dO[b, h]))
+            bQ[b, h] = s64 * (e @ np.abs(K[b, h]))
+            bK[b, h] = s64 * (e.T @ np.abs(Q[b, h]))
+    return bQ, bK, bV
