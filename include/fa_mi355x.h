@@ -28,7 +28,7 @@
 extern "C" {
 #endif
 
-#define FA_MI355X_ABI_VERSION 3
+#define FA_MI355X_ABI_VERSION 4
 
 typedef enum {
   FA_F32 = 0,   /* IEEE binary32 */
@@ -186,6 +186,43 @@ fa_status flash_attn_fwd_fp8(const void* q, const void* k, const void* v,
                              float scale, int causal,
                              float q_descale, float k_descale, float v_descale,
                              void* stream);
+
+/*
+ * flash_attn_bwd -- gradients of flash_attn_fwd with respect to q, k and v.
+ *
+ * Source: the pages imply training ("FlashAttention: Tiled & Fused") without
+ * giving the backward pass; it is the chain rule through flash_attn_fwd's
+ * definition ("FlashAttention", Chapter 15, "Standard vs Flash Attention"),
+ * tiled in the same way (the N x N matrices are recomputed tile by tile from
+ * q, k and the saved lse, never stored).  With P = exp(s - lse) the forward's
+ * softmax and do the gradient of the loss with respect to o:
+ *   dv = P^T do,  dP = do v^T,  D_i = sum_c do[i,c] o[i,c],
+ *   dS = P * (dP - D),  dq = scale * dS k,  dk = scale * dS^T q.
+ *
+ * Arguments: q, k, v, o, dout (do) device pointers to contiguous [B, H, N, d]
+ * arrays of `dtype` (FA_F16 or FA_BF16), o and lse as flash_attn_fwd wrote
+ * them (same scale and causal); dq, dk, dv contiguous [B, H, N, d] of
+ * `dtype`, fully overwritten; workspace: device scratch owned by the caller,
+ * 16-byte aligned, at least flash_attn_bwd_workspace_size(B, H, N) bytes (it
+ * receives D; its contents on entry do not matter).  B, H, N, d, scale,
+ * causal, stream as for flash_attn_fwd.  P and dS are rounded to `dtype`
+ * before the products that use them (accuracy contract: the per-element
+ * bound derived from those roundings and from o's).  Enqueues three kernels
+ * and returns without synchronising; dq, dk, dv and the workspace must not
+ * overlap the inputs or each other.  Errors as for flash_attn_fwd, plus
+ * FA_ERR_WORKSPACE.
+ */
+fa_status flash_attn_bwd(const void* q, const void* k, const void* v,
+                         const void* o, const void* dout, const float* lse,
+                         void* dq, void* dk, void* dv,
+                         int64_t B, int64_t H, int64_t N, int64_t d,
+                         float scale, int causal,
+                         void* workspace, int64_t workspace_bytes,
+                         fa_dtype dtype, void* stream);
+
+/* Workspace bytes flash_attn_bwd needs: B * H * N * 4 (0 for empty sizes, -1
+ * if that overflows).  No HIP call. */
+int64_t flash_attn_bwd_workspace_size(int64_t B, int64_t H, int64_t N);
 
 /* Key ranges flash_attn_fwd_kvcache uses for these sizes and num_splits (1
  * for empty or invalid sizes).  No HIP call. */

@@ -23,10 +23,10 @@ STATUS = {
     8: "FA_ERR_NO_DEVICE", 9: "FA_ERR_ARCH", 10: "FA_ERR_HIP", 11: "FA_ERR_WORKSPACE",
 }
 STATUS_CODE = {name: code for code, name in STATUS.items()}
-EXPORTS = ("flash_attn_fwd", "flash_attn_fwd_fp8", "flash_attn_fwd_kvcache", "flash_attn_kvcache_splits",
+EXPORTS = ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_workspace_size", "flash_attn_fwd_fp8", "flash_attn_fwd_kvcache", "flash_attn_kvcache_splits",
            "flash_attn_kvcache_workspace_size", "flash_attn_status_str",
            "flash_attn_last_error", "flash_attn_abi_version")
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 _lib = None
 _lock = threading.Lock()
@@ -57,6 +57,12 @@ def lib() -> ctypes.CDLL:
             L.flash_attn_fwd.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 4 + [
                 ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
             L.flash_attn_fwd.restype = ctypes.c_int
+            L.flash_attn_bwd.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int64] * 4 + [
+                ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                ctypes.c_void_p]
+            L.flash_attn_bwd.restype = ctypes.c_int
+            L.flash_attn_bwd_workspace_size.argtypes = [ctypes.c_int64] * 3
+            L.flash_attn_bwd_workspace_size.restype = ctypes.c_int64
             L.flash_attn_fwd_fp8.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 4 + [
                 ctypes.c_float, ctypes.c_int, ctypes.c_float, ctypes.c_float, ctypes.c_float,
                 ctypes.c_void_p]
@@ -275,3 +281,54 @@ def flash_attn_fwd_fp8(q, k, v, o=None, lse=None, *, q_descale: float, k_descale
     if st != 0:
         raise FlashAttnError(st, L.flash_attn_last_error().decode())
     return o, lse
+
+
+def flash_attn_bwd(q, k, v, o, lse, dout, dq=None, dk=None, dv=None, *,
+                   scale: Optional[float] = None, causal: bool = False, workspace=None,
+                   stream=None):
+    """Gradients (dq, dk, dv) of flash_attn_fwd for upstream gradient dout.
+
+    q, k, v, o, dout: contiguous [B, H, N, d] float16 or bfloat16 device
+    tensors (o and lse as flash_attn_fwd returned them for the same scale and
+    causal); dq, dk, dv optional preallocated outputs; workspace optional
+    device tensor of at least flash_attn_bwd_workspace_size(B, H, N) bytes
+    (allocated here when omitted).  Enqueued on `stream` (default: the current
+    stream of q's device) without synchronising.
+    """
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise ValueError(f"{name} must be a device tensor")
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor like q")
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    code = _dtype_code(q)
+    if (lse.shape != (B, H, N) or lse.dtype != torch.float32 or lse.device != q.device
+            or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor like q")
+    L = lib()
+    need = L.flash_attn_bwd_workspace_size(B, H, N)
+    if need < 0:
+        raise ValueError("workspace size overflows")
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    with torch.cuda.device(q.device):
+        s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        st = L.flash_attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                              dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                              dv.data_ptr(), B, H, N, d, float(scale), int(bool(causal)),
+                              workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                              code, s.cuda_stream)
+    if st != 0:
+        raise FlashAttnError(st, L.flash_attn_last_error().decode())
+    return dq, dk, dv

@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <cstring>
 
+#include "fa_bwd.h"
 #include "fa_fp8.h"
 #include "fa_kvcache.h"
 #include "fa_launch.h"
@@ -216,6 +217,86 @@ fa_status flash_attn_fwd_fp8(const void* q, const void* k, const void* v, void* 
   a.v_descale = v_descale;
   (void)hipGetLastError();
   const hipError_t e = fa::launch_forward_fp8(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
+int64_t flash_attn_bwd_workspace_size(int64_t B, int64_t H, int64_t N) {
+  if (B <= 0 || H <= 0 || N <= 0) return 0;
+  if (B > ((int64_t)1 << 40) / H || N > ((int64_t)1 << 40) / (B * H)) return -1;
+  return B * H * N * 4;
+}
+
+fa_status flash_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                         int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
+                         void* workspace, int64_t workspace_bytes, fa_dtype dtype, void* stream) {
+  g_last_error[0] = '\0';
+  if (B < 0 || H < 0 || N < 0)
+    return fail(FA_ERR_SHAPE, "B, H, N must be >= 0 (got %lld, %lld, %lld)", (long long)B,
+                (long long)H, (long long)N);
+  if (d != 64 && d != 128) return fail(FA_ERR_HEAD_DIM, "d must be 64 or 128 (got %lld)", (long long)d);
+  if (dtype != FA_F16 && dtype != FA_BF16)
+    return fail(FA_ERR_DTYPE, "the backward pass takes FA_F16 or FA_BF16 (got %d)", (int)dtype);
+  if (!std::isfinite(scale)) return fail(FA_ERR_SCALE, "scale must be finite");
+  if (B == 0 || H == 0 || N == 0) return FA_OK;
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv)
+    return fail(FA_ERR_NULL, "q, k, v, o, dout, lse, dq, dk and dv must be non-NULL");
+  const uintptr_t mis = ((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o |
+                         (uintptr_t)dout | (uintptr_t)lse | (uintptr_t)dq | (uintptr_t)dk |
+                         (uintptr_t)dv) & 15u;
+  if (mis) return fail(FA_ERR_ALIGN, "all tensors must be 16-byte aligned");
+  const int64_t kLimit = (int64_t)1 << 62;
+  if (B > kLimit / H || N > kLimit / (B * H) || d * 2 > kLimit / (B * H * N))
+    return fail(FA_ERR_SHAPE, "B*H*N*d*elem overflows");
+  const int64_t BH = B * H;
+  const int64_t n_blk = (N + fa::kBwdRowsPerWorkgroup - 1) / fa::kBwdRowsPerWorkgroup;
+  if (n_blk > INT32_MAX || BH * n_blk > (int64_t)UINT32_MAX / fa::kBwdThreads ||
+      BH * N > (int64_t)UINT32_MAX / 16)
+    return fail(FA_ERR_SHAPE, "B*H*ceil(N/%d) = %lld workgroups exceeds the grid limit",
+                fa::kBwdRowsPerWorkgroup, (long long)(BH * n_blk));
+  const int64_t need = BH * N * 4;
+  if (!workspace) return fail(FA_ERR_WORKSPACE, "the backward pass needs a workspace of %lld bytes", (long long)need);
+  if ((uintptr_t)workspace & 15u) return fail(FA_ERR_ALIGN, "workspace must be 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE, "workspace has %lld bytes, the backward pass needs %lld",
+                (long long)workspace_bytes, (long long)need);
+  const int64_t tb = BH * N * d * 2, lb = BH * N * 4;
+  const void* ins[6] = {q, k, v, o, dout, lse};
+  const int64_t in_bytes[6] = {tb, tb, tb, tb, tb, lb};
+  void* outs[4] = {dq, dk, dv, workspace};
+  const int64_t out_bytes[4] = {tb, tb, tb, need};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlaps(outs[i], out_bytes[i], ins[j], in_bytes[j]))
+        return fail(FA_ERR_ALIAS, "dq, dk, dv and the workspace must not overlap an input");
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(outs[i], out_bytes[i], outs[j], out_bytes[j]))
+        return fail(FA_ERR_ALIAS, "dq, dk, dv and the workspace must not overlap each other");
+  }
+
+  fa_status st = check_device();
+  if (st != FA_OK) return st;
+
+  fa::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.workspace = workspace;
+  a.BH = BH;
+  a.N = N;
+  a.d = (int)d;
+  a.scale = scale;
+  a.causal = causal != 0;
+  a.dtype = (fa::Dtype)dtype;
+  (void)hipGetLastError();
+  const hipError_t e = fa::launch_backward(a, (hipStream_t)stream);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return FA_OK;
 }

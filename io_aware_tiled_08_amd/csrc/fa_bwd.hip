@@ -1,0 +1,508 @@
+// FlashAttention backward pass for fp16 and bf16 on gfx950.
+//
+// What is computed: the gradients of the forward pass O = softmax(scale Q K^T) V
+// (causal or not) for an upstream gradient dO, from Q, K, V, O, dO and the
+// forward's LSE.  With P = exp(scale Q K^T - LSE) (the forward's softmax,
+// recomputed tile by tile from the saved row statistics, never stored):
+//   dV = P^T dO,  dP = dO V^T,  D = rowsum(dO * O),  dS = P * (dP - D),
+//   dQ = scale dS K,  dK = scale dS^T Q.
+// The pages only imply training ("FlashAttention: Tiled & Fused"); the
+// gradient is the chain rule through the forward's definition ("FlashAttention"
+// chapter 15, "Standard vs Flash Attention"), and the tiling follows the
+// forward's idea: K/V (or Q/dO) tiles staged on chip, the N x N matrices never
+// written to HBM.
+//
+// Three kernels, no atomics:
+//   * bwd_prep: D = rowsum(dO * O) per row, fp32, into the workspace.
+//   * bwd_dkdv: a workgroup owns 128 keys (4 waves x 32); it walks 64-query
+//     tiles of Q and dO (with their LSE and D) through LDS and accumulates
+//     dV^T += dO^T P and dK^T += Q^T dS in registers.  Scores are computed as
+//     S = Q K^T with K in registers, so a lane owns one key and the 16 queries
+//     of a 32x32 block sit in its registers; P and dS then feed the next
+//     products as B operands straight from those registers.
+//   * bwd_dq: a workgroup owns 128 queries; it walks 64-key tiles of K and V
+//     and accumulates dQ^T += K^T dS^T with S^T = K Q^T (lane = query, as in the
+//     forward kernel).
+// Every tile is read both by rows (MFMA A operands) and transposed
+// (ds_read_b64_tr_b16, for the d x rows operands); one XOR permutation of the
+// 16-byte chunks of a row serves both without LDS bank conflicts.
+#include "fa_bwd.h"
+#include "fa_device.h"
+#include "fa_f16_common.h"
+
+namespace fa {
+namespace {
+
+constexpr int kBwdRows = 128;  // keys (dK/dV kernel) or queries (dQ kernel) per workgroup
+constexpr int kBwdTile = 64;   // queries or keys per staged tile
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;  // workspace: D per row
+  int64_t N;
+  int32_t n_blk;  // 128-row blocks per (b, h)
+  float c;        // scale * log2(e)
+  float scale;
+};
+
+// Chunk c of row r sits at slot c ^ f(r).  Row reads (16 lanes: one chunk of
+// 16 rows distinct mod 16) and transposing reads (32 lanes: 4 chunks of 4
+// aligned rows) both hit 16 distinct 16-byte bank groups.
+template <int D>
+__device__ __forceinline__ constexpr int bswz(int r, int c) {
+  return D == 128 ? c ^ (((r & 3) << 2) | ((r >> 2) & 3))
+                  : c ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
+// ---- D = rowsum(dO * O) ------------------------------------------------------
+template <typename T, int D>
+__global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams p, int64_t rows) {
+  constexpr int TPR = D / 8;         // threads per row, 8 elements each
+  const int64_t row = (int64_t)blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+  const int c8 = threadIdx.x % TPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4 a = *(const u32x4*)((const T*)p.dout + row * D + 8 * c8);
+    const u32x4 b = *(const u32x4*)((const T*)p.o + row * D + 8 * c8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const auto x = bits<typename Half<T>::Pair>(a[i]);
+      const auto y = bits<typename Half<T>::Pair>(b[i]);
+      acc += (float)x[0] * (float)y[0] + (float)x[1] * (float)y[1];
+    }
+  }
+#pragma unroll
+  for (int w = TPR / 2; w > 0; w >>= 1) acc += __shfl_xor(acc, w, TPR);
+  if (row < rows && c8 == 0) p.delta[row] = acc;
+}
+
+// Row-read and transposing-read helpers over a staged [kBwdTile x D] tile.
+template <typename T, int D>
+struct TileOps {
+  using Frag = typename Half<T>::Frag;
+  static constexpr int RB = 2 * D;
+  // A operand row fragment: row r, chunk c (8 elements).
+  static __device__ __forceinline__ Frag row(const char* tile, int r, int c) {
+    return bits<Frag>(*(const u32x4*)(tile + r * RB + bswz<D>(r, c) * 16));
+  }
+  // Transposed A operand: d rows db*32 + (lane column), 8 tile rows
+  // r0 + 8*hh + 0..7 (r0 a multiple of 16) for lane half hh.
+  static __device__ __forceinline__ Frag rows_t(const char* tile, int r0, int db, int lane) {
+    const int g = lane >> 4, j = lane & 15, hh = lane >> 5;
+    const int col = db * 32 + 16 * (g & 1) + 4 * (j & 3);
+    const int c = col >> 3, off = (col & 7) * 2;
+    const int ra = r0 + 8 * hh + (j >> 2), rb = ra + 4;
+    const u32x2 lo = lds_read_tr(tile, ra * RB + bswz<D>(ra, c) * 16 + off);
+    const u32x2 hi = lds_read_tr(tile, rb * RB + bswz<D>(rb, c) * 16 + off);
+    return bits<Frag>(u32x4{lo[0], lo[1], hi[0], hi[1]});
+  }
+};
+
+// Stage rows [r0, r0 + kBwdTile) of a [N, D] head into an LDS tile: the four
+// waves each issue kBwdTile*2D/1024/4 loads of 1 KiB; rows past N read zero.
+template <int D>
+__device__ __forceinline__ void stage_tile(const void* head, int64_t r0, int64_t N, uint32_t lds,
+                                           int wave, int lane) {
+  constexpr int RB = 2 * D, CPR = D / 8, RPL = 1024 / RB;
+  constexpr int LPW = kBwdTile * RB / 1024 / 4;
+  const uint32_t rows = (uint32_t)(N - r0 < kBwdTile ? N - r0 : kBwdTile);
+  const u32x4 rs = buffer_rsrc((const char*)head + r0 * RB, rows * RB);
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int r = (wave * LPW + j) * RPL + lane / CPR;
+    const int slot = lane % CPR;
+    dma_load16(rs, lds + (wave * LPW + j) * 1024, r * RB + bswz<D>(r, slot) * 16);
+  }
+}
+
+// Wait until at most n of this wave's loads are outstanding (vmcnt(n), gfx9
+// encoding); no memory access moves across the wait.
+template <int n>
+__device__ __forceinline__ void wait_loads() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (n & 15) | ((n >> 4) << 14));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+__device__ __forceinline__ void block_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// ---- dK, dV ------------------------------------------------------------------
+template <typename T, int D, bool CAUSAL>
+__global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p) {
+  using H = Half<T>;
+  using Frag = typename H::Frag;
+  using Pair = typename H::Pair;
+  using Ops = TileOps<T, D>;
+  constexpr int RB = 2 * D;
+  constexpr int TILE = kBwdTile * RB;
+  constexpr int NKS = D / 16;
+  constexpr int ND = D / 32;
+  __shared__ __attribute__((aligned(1024))) char smem[2][2][TILE];  // [buffer][Q, dO]
+  __shared__ __attribute__((aligned(16))) float stat[2][2][kBwdTile];  // [buffer][LSE, D]
+
+  const int64_t N = p.N;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+  // Causal blocks with the most queries (lowest keys) first.
+  const int64_t bh = blockIdx.x / p.n_blk;
+  const int kblk = blockIdx.x % p.n_blk;
+  const int64_t k0 = (int64_t)kblk * kBwdRows;
+  const int64_t kw = k0 + 32 * wave;  // this wave's first key
+  const int64_t key = kw + l32;       // this lane's key (B-operand column)
+
+  const T* Qh = (const T*)p.q + bh * N * D;
+  const T* Kh = (const T*)p.k + bh * N * D;
+  const T* Vh = (const T*)p.v + bh * N * D;
+  const T* dOh = (const T*)p.dout + bh * N * D;
+  const float* Lh = p.lse + bh * N;
+  const float* Dh = p.delta + bh * N;
+
+  // K and V of this lane's key (B operands of S = Q K^T and dP = dO V^T).
+  Frag kf[NKS], vf[NKS];
+  {
+    const bool ok = key < N;
+    const T* ks_ = Kh + (ok ? key : 0) * D + 8 * hh;
+    const T* vs_ = Vh + (ok ? key : 0) * D + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      kf[ks] = bits<Frag>(ok ? *(const u32x4*)(ks_ + 16 * ks) : u32x4{0, 0, 0, 0});
+      vf[ks] = bits<Frag>(ok ? *(const u32x4*)(vs_ + 16 * ks) : u32x4{0, 0, 0, 0});
+    }
+  }
+
+  // Query tiles: causal blocks start at the first tile holding a query >= k0.
+  const int qt_begin = CAUSAL ? (int)(k0 / kBwdTile) : 0;
+  const int qt_end = (int)((N + kBwdTile - 1) / kBwdTile);
+  const uint32_t lds_base = lds_addr(&smem[0][0][0]);
+  const uint32_t stat_base = lds_addr(&stat[0][0][0]);
+  auto issue = [&](int qt) {
+    if (qt >= qt_end) return;
+    const int buf = qt & 1;
+    const int64_t r0 = (int64_t)qt * kBwdTile;
+    stage_tile<D>(Qh + r0 * D, 0, N - r0, lds_base + (buf * 2 + 0) * TILE, wave, lane);
+    stage_tile<D>(dOh + r0 * D, 0, N - r0, lds_base + (buf * 2 + 1) * TILE, wave, lane);
+    if (wave == 0 && lane < 16) {  // 64 floats each: 16 lanes x 16 bytes
+      const uint32_t rows = (uint32_t)(N - r0 < kBwdTile ? N - r0 : kBwdTile);
+      dma_load16(buffer_rsrc(Lh + r0, rows * 4), stat_base + (buf * 2 + 0) * kBwdTile * 4, lane * 16);
+      dma_load16(buffer_rsrc(Dh + r0, rows * 4), stat_base + (buf * 2 + 1) * kBwdTile * 4, lane * 16);
+    }
+  };
+
+  f32x16 dk[ND], dv[ND];
+#pragma unroll
+  for (int db = 0; db < ND; ++db) dk[db] = dv[db] = f32x16{};
+  const float c = p.c;
+  const int krow = k_row_of_lane(l32);
+
+  // The register loads above must land now: the compiler does not count the
+  // tile loads, so a wait it placed inside the loop would drain the prefetch.
+  issue(qt_begin);
+  wait_loads<0>();
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    fence(kf[ks]);
+    fence(vf[ks]);
+  }
+  constexpr int LPW = TILE / 1024 / 4;  // loads per wave per tensor per tile
+  for (int qt = qt_begin; qt < qt_end; ++qt) {
+    // Tile qt + 1 is loaded while tile qt is used; wave 0 also loads the
+    // tile's LSE and D.
+    if (qt + 1 < qt_end) {
+      issue(qt + 1);
+      if (wave == 0)
+        wait_loads<2 * LPW + 2>();
+      else
+        wait_loads<2 * LPW>();
+    } else {
+      wait_loads<0>();
+    }
+    block_barrier();
+    const int buf = qt & 1;
+    const char* qtile = &smem[buf][0][0];
+    const char* dotile = &smem[buf][1][0];
+    const float* lse_t = &stat[buf][0][0];
+    const float* d_t = &stat[buf][1][0];
+    const int64_t q0 = (int64_t)qt * kBwdTile;
+#pragma unroll
+    for (int qb = 0; qb < kBwdTile / 32; ++qb) {
+      const int64_t qbase = q0 + 32 * qb;
+      if (CAUSAL && qbase + 31 < kw) continue;  // every query of the block precedes the wave's keys
+      if (qbase >= N) continue;
+      // S = Q K^T, dP = dO V^T: register r of the lane holds query
+      // qbase + key_of_reg(r, hh) and key `key` (A rows fed permuted).
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        s = H::mma(Ops::row(qtile, 32 * qb + krow, 2 * ks + hh), kf[ks], s);
+        dp = H::mma(Ops::row(dotile, 32 * qb + krow, 2 * ks + hh), vf[ks], dp);
+      }
+      float lse2[16], dl[16];
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int qi = 32 * qb + 16 * half + 8 * hh;  // 8 consecutive queries
+        const float4 a0 = *(const float4*)(lse_t + qi), a1 = *(const float4*)(lse_t + qi + 4);
+        const float4 b0 = *(const float4*)(d_t + qi), b1 = *(const float4*)(d_t + qi + 4);
+        const float la[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        const float lb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          lse2[8 * half + e] = la[e] * kLog2e;
+          dl[8 * half + e] = lb[e];
+        }
+      }
+      Frag pf[2], sf[2];
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        u32x4 fp, fs;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float pv[2], sv[2];
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            const int r = 8 * jj + 2 * e + x;
+            const int64_t qi = qbase + key_of_reg(r, hh);
+            const bool vis = qi < N && key < N && (!CAUSAL || key <= qi);
+            const float pr = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2[r])) : 0.f;
+            pv[x] = pr;
+            sv[x] = pr * (dp[r] - dl[r]);
+          }
+          fp[e] = bits<uint32_t>(H::pack(pv[0], pv[1]));
+          fs[e] = bits<uint32_t>(H::pack(sv[0], sv[1]));
+        }
+        pf[jj] = bits<Frag>(fp);
+        sf[jj] = bits<Frag>(fs);
+      }
+      // dV^T += dO^T P, dK^T += Q^T dS (A operands: transposed tile reads).
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int db = 0; db < ND; ++db) {
+          dv[db] = H::mma(Ops::rows_t(dotile, 32 * qb + 16 * jj, db, lane), pf[jj], dv[db]);
+          dk[db] = H::mma(Ops::rows_t(qtile, 32 * qb + 16 * jj, db, lane), sf[jj], dk[db]);
+        }
+    }
+    block_barrier();  // the buffer is refilled two tiles later
+  }
+
+  // dK = scale * dK^T^T, dV: lane `key`, register r of block db is d row
+  // db*32 + 8*(r/4) + 4*hh + r%4.
+  if (key < N) {
+    T* dkd = (T*)p.dk + (bh * N + key) * D + 4 * hh;
+    T* dvd = (T*)p.dv + (bh * N + key) * D + 4 * hh;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const Pair a = H::pack(dk[db][4 * g] * p.scale, dk[db][4 * g + 1] * p.scale);
+        const Pair b = H::pack(dk[db][4 * g + 2] * p.scale, dk[db][4 * g + 3] * p.scale);
+        *(u32x2*)(dkd + db * 32 + 8 * g) = u32x2{bits<uint32_t>(a), bits<uint32_t>(b)};
+        const Pair e = H::pack(dv[db][4 * g], dv[db][4 * g + 1]);
+        const Pair f = H::pack(dv[db][4 * g + 2], dv[db][4 * g + 3]);
+        *(u32x2*)(dvd + db * 32 + 8 * g) = u32x2{bits<uint32_t>(e), bits<uint32_t>(f)};
+      }
+  }
+}
+
+// ---- dQ ----------------------------------------------------------------------
+template <typename T, int D, bool CAUSAL>
+__global__ void __launch_bounds__(256, 1) bwd_dq_kernel(BwdParams p) {
+  using H = Half<T>;
+  using Frag = typename H::Frag;
+  using Pair = typename H::Pair;
+  using Ops = TileOps<T, D>;
+  constexpr int RB = 2 * D;
+  constexpr int TILE = kBwdTile * RB;
+  constexpr int NKS = D / 16;
+  constexpr int ND = D / 32;
+  __shared__ __attribute__((aligned(1024))) char smem[2][2][TILE];  // [buffer][K, V]
+
+  const int64_t N = p.N;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hh = lane >> 5;
+  // Causal: the longest query blocks (highest index) first.
+  const int64_t bh = blockIdx.x / p.n_blk;
+  int qblk = blockIdx.x % p.n_blk;
+  if (CAUSAL) qblk = p.n_blk - 1 - qblk;
+  const int64_t q0 = (int64_t)qblk * kBwdRows;
+  const int64_t qw = q0 + 32 * wave;
+  const int64_t qrow = qw + l32;
+
+  const T* Qh = (const T*)p.q + bh * N * D;
+  const T* Kh = (const T*)p.k + bh * N * D;
+  const T* Vh = (const T*)p.v + bh * N * D;
+  const T* dOh = (const T*)p.dout + bh * N * D;
+
+  // Q and dO of this lane's query (B operands of S^T = K Q^T, dP^T = V dO^T).
+  Frag qf[NKS], df[NKS];
+  float lse2 = 0.f, drow = 0.f;
+  {
+    const bool ok = qrow < N;
+    const T* qs_ = Qh + (ok ? qrow : 0) * D + 8 * hh;
+    const T* ds_ = dOh + (ok ? qrow : 0) * D + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      qf[ks] = bits<Frag>(ok ? *(const u32x4*)(qs_ + 16 * ks) : u32x4{0, 0, 0, 0});
+      df[ks] = bits<Frag>(ok ? *(const u32x4*)(ds_ + 16 * ks) : u32x4{0, 0, 0, 0});
+    }
+    if (ok) {
+      lse2 = p.lse[bh * N + qrow] * kLog2e;
+      drow = p.delta[bh * N + qrow];
+    }
+  }
+
+  const int64_t kv_end = CAUSAL ? (q0 + kBwdRows < N ? q0 + kBwdRows : N) : N;
+  const int n_tiles = (int)((kv_end + kBwdTile - 1) / kBwdTile);
+  const int64_t wave_end = CAUSAL ? (qw + 32 < N ? qw + 32 : N) : N;
+  const int wave_tiles = qw < N ? (int)((wave_end + kBwdTile - 1) / kBwdTile) : 0;
+  const uint32_t lds_base = lds_addr(&smem[0][0][0]);
+  auto issue = [&](int t) {
+    if (t >= n_tiles) return;
+    const int buf = t & 1;
+    const int64_t r0 = (int64_t)t * kBwdTile;
+    stage_tile<D>(Kh + r0 * D, 0, N - r0, lds_base + (buf * 2 + 0) * TILE, wave, lane);
+    stage_tile<D>(Vh + r0 * D, 0, N - r0, lds_base + (buf * 2 + 1) * TILE, wave, lane);
+  };
+
+  f32x16 dq[ND];
+#pragma unroll
+  for (int db = 0; db < ND; ++db) dq[db] = f32x16{};
+  const float c = p.c;
+  const int krow = k_row_of_lane(l32);
+
+  issue(0);
+  wait_loads<0>();
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    fence(qf[ks]);
+    fence(df[ks]);
+  }
+  fence(lse2);
+  fence(drow);
+  constexpr int LPW = TILE / 1024 / 4;
+  for (int t = 0; t < n_tiles; ++t) {
+    if (t + 1 < n_tiles) {
+      issue(t + 1);
+      wait_loads<2 * LPW>();
+    } else {
+      wait_loads<0>();
+    }
+    block_barrier();
+    if (t < wave_tiles) {
+      const int buf = t & 1;
+      const char* ktile = &smem[buf][0][0];
+      const char* vtile = &smem[buf][1][0];
+      const int64_t k0 = (int64_t)t * kBwdTile;
+#pragma unroll
+      for (int kb = 0; kb < kBwdTile / 32; ++kb) {
+        // S^T = K Q^T and dP^T = V dO^T: register r holds key
+        // k0 + 32*kb + key_of_reg(r, hh) of this lane's query.
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          s = H::mma(Ops::row(ktile, 32 * kb + krow, 2 * ks + hh), qf[ks], s);
+          dp = H::mma(Ops::row(vtile, 32 * kb + krow, 2 * ks + hh), df[ks], dp);
+        }
+        Frag sf[2];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          u32x4 fs;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float sv[2];
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+              const int r = 8 * jj + 2 * e + x;
+              const int64_t kj = k0 + 32 * kb + key_of_reg(r, hh);
+              const bool vis = kj < N && qrow < N && (!CAUSAL || kj <= qrow);
+              const float pr = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2)) : 0.f;
+              sv[x] = pr * (dp[r] - drow);
+            }
+            fs[e] = bits<uint32_t>(H::pack(sv[0], sv[1]));
+          }
+          sf[jj] = bits<Frag>(fs);
+        }
+        // dQ^T += K^T dS^T.
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int db = 0; db < ND; ++db)
+            dq[db] = H::mma(Ops::rows_t(ktile, 32 * kb + 16 * jj, db, lane), sf[jj], dq[db]);
+      }
+    }
+    block_barrier();
+  }
+
+  if (qrow < N) {
+    T* dst = (T*)p.dq + (bh * N + qrow) * D + 4 * hh;
+#pragma unroll
+    for (int db = 0; db < ND; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const Pair a = H::pack(dq[db][4 * g] * p.scale, dq[db][4 * g + 1] * p.scale);
+        const Pair b = H::pack(dq[db][4 * g + 2] * p.scale, dq[db][4 * g + 3] * p.scale);
+        *(u32x2*)(dst + db * 32 + 8 * g) = u32x2{bits<uint32_t>(a), bits<uint32_t>(b)};
+      }
+  }
+}
+
+template <typename T, int D, bool CAUSAL>
+hipError_t launch(const BwdArgs& a, hipStream_t stream) {
+  BwdParams p;
+  p.q = a.q;
+  p.k = a.k;
+  p.v = a.v;
+  p.o = a.o;
+  p.dout = a.dout;
+  p.lse = a.lse;
+  p.dq = a.dq;
+  p.dk = a.dk;
+  p.dv = a.dv;
+  p.delta = (float*)a.workspace;
+  p.N = a.N;
+  p.n_blk = (int32_t)((a.N + kBwdRows - 1) / kBwdRows);
+  p.c = a.scale * kLog2e;
+  p.scale = a.scale;
+  const int64_t rows = a.BH * a.N;
+  constexpr int RPB = 256 / (D / 8);
+  hipLaunchKernelGGL((bwd_prep_kernel<T, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
+                     stream, p, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const unsigned grid = (unsigned)(a.BH * p.n_blk);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3(grid), dim3(256), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3(grid), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_t(const BwdArgs& a, hipStream_t s) {
+  if (a.d == 64) return a.causal ? launch<T, 64, true>(a, s) : launch<T, 64, false>(a, s);
+  return a.causal ? launch<T, 128, true>(a, s) : launch<T, 128, false>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_backward(const BwdArgs& a, hipStream_t stream) {
+  return a.dtype == Dtype::BF16 ? launch_t<__bf16>(a, stream) : launch_t<_Float16>(a, stream);
+}
+
+}  // namespace fa

@@ -34,7 +34,7 @@ DTYPES = {
 }
 ELEM_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
 
-TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_ROWS = 0, 1, 2, 3
+TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_ROWS, TENSOR_DOUT = 0, 1, 2, 3, 4
 
 
 @dataclasses.dataclass(frozen=True)
@@ -339,3 +339,10 @@ FP8_WORKLOADS = {
 
 def fp8_workload_inputs(w: Fp8Workload):
     return random_qkv_fp8(w.B, w.H, w.N, w.d, w.seed)
+
+
+def random_dout(B: int, H: int, N: int, d: int, dtype: str, seed: int) -> torch.Tensor:
+    """Upstream gradient dO [B, H, N, d], iid N(0,1), same recipe as
+    random_qkv with tensor id 4."""
+    return _draw(seed, TENSOR_DOUT, B, H, N, d, dtype,
+                 lambda rng, b, h: rng.standard_normal((N, d), dtype=np.float32))

@@ -1,0 +1,96 @@
+"""Backward pass (flash_attn_bwd) vs the fp64 oracle (needs a gfx950 GPU).
+
+The kernel receives the forward output O rounded to the input type and the
+exact LSE in float32, as flash_attn_fwd would hand them over.  Accuracy
+contract (oracle.backward_error_bound): the bound per element that follows
+from rounding P, dS and O to the input type (unit u = 2^-11 for fp16, 2^-8
+for bf16), plus the rounding of dq, dk, dv themselves (u |ref|) and fp32
+accumulation (1e-5 max|ref| + 1e-6).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from io_aware_tiled_08_amd import FlashAttnError, flash_attn_bwd
+from io_aware_tiled_08_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+UNIT = {"f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+
+
+def run_bwd(q, k, v, do, scale, causal, dtype, stream=None):
+    O, L = oracle.attention_forward(q, k, v, scale, causal)
+    tdt = W.DTYPES[dtype]
+    o = torch.from_numpy(O).to(tdt).to(DEV)
+    lse = torch.from_numpy(L).to(torch.float32).to(DEV)
+    qd, kd, vd, dod = (x.to(DEV) for x in (q, k, v, do))
+    dq, dk, dv = (torch.full_like(qd, float("nan")) for _ in range(3))
+    flash_attn_bwd(qd, kd, vd, o, lse, dod, dq, dk, dv, scale=scale, causal=causal, stream=stream)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def check(got, q, k, v, do, scale, causal, dtype, label):
+    u = UNIT[dtype]
+    refs = oracle.attention_backward(q, k, v, do, scale, causal)[:3]
+    bounds = oracle.backward_error_bound(q, k, v, do, scale, causal, u=u)
+    for name, g, ref, b in zip(("dQ", "dK", "dV"), got, refs, bounds):
+        G = g.double().cpu().numpy()
+        assert np.isfinite(G).all(), f"{label} {name}: non-finite"
+        tol = 1.2 * b + u * np.abs(ref) + 1e-5 * max(1.0, float(np.abs(ref).max())) + 1e-6
+        err = np.abs(G - ref)
+        print(f"{label} {name}: max|d|={err.max():.3e} max|ref|={np.abs(ref).max():.3e} "
+              f"max err/tol={float((err / tol).max()):.3f}", flush=True)
+        assert np.all(err <= tol), f"{label} {name}: outside the 16-bit backward bound"
+
+
+@pytest.mark.parametrize("N", [1, 17, 64, 65, 127, 128, 129, 200, 256, 300])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_backward_sweep(dtype, d, causal, N):
+    q, k, v = W.random_qkv(1, 2, N, d, dtype, seed=7000 + N)
+    do = W.random_dout(1, 2, N, d, dtype, seed=7000 + N)
+    scale = W.default_scale(d)
+    got = run_bwd(q, k, v, do, scale, causal, dtype)
+    check(got, q, k, v, do, scale, causal, dtype, f"{dtype} d={d} causal={causal} N={N}")
+
+
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 0.5])
+def test_backward_batch_heads_and_scales(scale):
+    q, k, v = W.random_qkv(2, 3, 150, 64, "f16", seed=7100)
+    do = W.random_dout(2, 3, 150, 64, "f16", seed=7100)
+    for causal in (False, True):
+        got = run_bwd(q, k, v, do, scale, causal, "f16")
+        check(got, q, k, v, do, scale, causal, "f16", f"B=2 H=3 scale={scale} causal={causal}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_many_tiles(causal):
+    q, k, v = W.random_qkv(1, 4, 1000, 128, "bf16", seed=7200)
+    do = W.random_dout(1, 4, 1000, 128, "bf16", seed=7200)
+    got = run_bwd(q, k, v, do, W.default_scale(128), causal, "bf16")
+    check(got, q, k, v, do, W.default_scale(128), causal, "bf16", f"N=1000 causal={causal}")
+
+
+def test_backward_deterministic_and_side_stream():
+    q, k, v = W.random_qkv(1, 2, 333, 128, "f16", seed=7300)
+    do = W.random_dout(1, 2, 333, 128, "f16", seed=7300)
+    a = run_bwd(q, k, v, do, 0.088, True, "f16")
+    b = run_bwd(q, k, v, do, 0.088, True, "f16", stream=torch.cuda.Stream())
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_backward_workspace_and_dtype_errors():
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.float16, device=DEV)
+    lse = torch.zeros(1, 1, 8, dtype=torch.float32, device=DEV)
+    with pytest.raises(FlashAttnError, match="FA_ERR_WORKSPACE"):
+        flash_attn_bwd(x, x, x, x, lse, x, workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
+    y = x.float()
+    with pytest.raises(FlashAttnError, match="FA_ERR_DTYPE"):
+        flash_attn_bwd(y, y, y, y, lse, y)
