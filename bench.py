@@ -48,13 +48,15 @@ KERNEL_SOURCES = {
     "f32": ("fa_fwd_f32.hip", "fa_device.h"),
     "kvcache": ("fa_fwd_kvcache.hip", "fa_f16_common.h", "fa_device.h"),
     "fp8": ("fa_fwd_fp8.hip", "fa_f16_common.h", "fa_device.h"),
+    "bwd": ("fa_bwd.hip", "fa_f16_common.h", "fa_device.h"),
 }
 # (dominant kernel, every kernel of one call) name patterns in rocprofv3 output
 KERNEL_NAME_PATTERN = {"f16": ("fwd_f16_kernel", "fwd_f16_kernel"),
                        "bf16": ("fwd_f16_kernel", "fwd_f16_kernel"),
                        "f32": ("fwd_f32_kernel", "fwd_f32_kernel"),
                        "kvcache": ("kvcache_fwd_kernel", "kvcache_"),
-                       "fp8": ("fwd_fp8_kernel", "fwd_fp8_kernel")}
+                       "fp8": ("fwd_fp8_kernel", "fwd_fp8_kernel"),
+                       "bwd": ("bwd_dkdv_kernel", "bwd_")}
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 512 << 20  # one calibration copy: 512 MiB read + 512 MiB written
 COPY_REPS = 3
@@ -83,8 +85,11 @@ def workload_by_name(name: str):
         return W.CACHE_WORKLOADS[name], "kvcache"
     if name in W.FP8_WORKLOADS:
         return W.FP8_WORKLOADS[name], "fp8"
+    if name in W.BWD_WORKLOADS:
+        return W.BWD_WORKLOADS[name], "bwd"
     raise SystemExit(f"unknown workload {name!r}; known: "
-                     f"{sorted(W.WORKLOADS) + sorted(W.CACHE_WORKLOADS) + sorted(W.FP8_WORKLOADS)}")
+                     f"{sorted(W.WORKLOADS) + sorted(W.CACHE_WORKLOADS) + sorted(W.FP8_WORKLOADS)}"
+                     f" + {sorted(W.BWD_WORKLOADS)}")
 
 
 def traffic_path(workload: str) -> str:
@@ -340,6 +345,38 @@ def cpu_baseline_cache(w, q, k, v, budget_s: float):
     }
 
 
+def cpu_baseline_bwd(w, q, k, v, do, budget_s: float):
+    """Times the fp64 backward oracle one (b, h) head at a time until the
+    budget is spent (at least one head); FLOPs as the workload counts them."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()
+                       if p.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    heads = 0
+    t0 = time.perf_counter()
+    for b in range(w.B):
+        for h in range(w.H):
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            oracle.attention_backward(q[sl], k[sl], v[sl], do[sl], w.scale, w.causal)
+            heads += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        else:
+            continue
+        break
+    el = time.perf_counter() - t0
+    return {
+        "value": w.flops() * heads / (w.B * w.H) / el / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{heads} of {w.B * w.H} (b,h) heads of {w.name}, whole heads, fp64 numpy, {el:.1f} s",
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -391,6 +428,19 @@ def main():
         def step():
             flash_attn_fwd_kvcache(qd, kd, vd, o, lse, scale=w.scale, causal=w.causal,
                                    workspace=ws, stream=stream)
+    elif key == "bwd":
+        from io_aware_tiled_08_amd import flash_attn_bwd
+        q, k, v = W.random_qkv(w.B, w.H, w.N, w.d, w.dtype, w.seed)
+        do = W.random_dout(w.B, w.H, w.N, w.d, w.dtype, w.seed)
+        qd, kd, vd, dod = (x.to(dev) for x in (q, k, v, do))
+        o, lse = flash_attn_fwd(qd, kd, vd, scale=w.scale, causal=w.causal)
+        dq, dk, dv = (torch.empty_like(qd) for _ in range(3))
+        ws = torch.empty(max(binding.lib().flash_attn_bwd_workspace_size(w.B, w.H, w.N), 16),
+                         dtype=torch.uint8, device=dev)
+
+        def step():
+            flash_attn_bwd(qd, kd, vd, o, lse, dod, dq, dk, dv, scale=w.scale, causal=w.causal,
+                           workspace=ws, stream=stream)
     elif key == "fp8":
         from io_aware_tiled_08_amd import flash_attn_fwd_fp8
         q, k, v, qs, ks, vs = W.fp8_workload_inputs(w)
@@ -525,6 +575,8 @@ def main():
             roofline["frac_at_measured_clock"] = round(tflops / (peak * mhz / PEAK_CLOCK_MHZ), 4)
         result = {
             "metric": ("attention fwd TFLOP/s and % of MFMA peak, e4m3 inputs (1 GPU)" if key == "fp8"
+                       else "attention bwd TFLOP/s (2.5x the forward's FLOPs) and % of MFMA peak (1 GPU)"
+                       if key == "bwd"
                        else "attention fwd TFLOP/s and % of MFMA peak, N=4096 d=128 fp16 (1 GPU)"),
             "value": round(tflops, 2),
             "unit": "TFLOP/s",
@@ -547,6 +599,8 @@ def main():
     if args.cpu_budget > 0:
         if cache:
             result["cpu_baseline"] = cpu_baseline_cache(w, q, k, v, args.cpu_budget)
+        elif key == "bwd":
+            result["cpu_baseline"] = cpu_baseline_bwd(w, q, k, v, do, args.cpu_budget)
         elif key == "fp8":
             import oracle
             qx, kx, vx = (oracle.dequantize_fp8(x, s) for x, s in ((q, qs), (k, ks), (v, vs)))

@@ -123,6 +123,13 @@ __device__ __forceinline__ void stage_tile(const void* head, int64_t r0, int64_t
   }
 }
 
+// Workgroup i runs on XCD i % 8: give each XCD a contiguous range of the
+// logical blocks so that a head's blocks share one L2.
+__device__ __forceinline__ int xcd_order() {
+  const int n = gridDim.x, wg = blockIdx.x;
+  return (n % 8 == 0) ? (wg % 8) * (n / 8) + wg / 8 : wg;
+}
+
 // Wait until at most n of this wave's loads are outstanding (vmcnt(n), gfx9
 // encoding); no memory access moves across the wait.
 template <int n>
@@ -159,9 +166,11 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
-  // Causal blocks with the most queries (lowest keys) first.
-  const int64_t bh = blockIdx.x / p.n_blk;
-  const int kblk = blockIdx.x % p.n_blk;
+  // XCD-aware order (the blocks of one head share an XCD's L2); causal:
+  // the blocks with the most queries (lowest keys) first.
+  const int logical = xcd_order();
+  const int64_t bh = logical / p.n_blk;
+  const int kblk = logical % p.n_blk;
   const int64_t k0 = (int64_t)kblk * kBwdRows;
   const int64_t kw = k0 + 32 * wave;  // this wave's first key
   const int64_t key = kw + l32;       // this lane's key (B-operand column)
@@ -336,9 +345,10 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(BwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hh = lane >> 5;
-  // Causal: the longest query blocks (highest index) first.
-  const int64_t bh = blockIdx.x / p.n_blk;
-  int qblk = blockIdx.x % p.n_blk;
+  // XCD-aware order; causal: the longest query blocks (highest index) first.
+  const int logical = xcd_order();
+  const int64_t bh = logical / p.n_blk;
+  int qblk = logical % p.n_blk;
   if (CAUSAL) qblk = p.n_blk - 1 - qblk;
   const int64_t q0 = (int64_t)qblk * kBwdRows;
   const int64_t qw = q0 + 32 * wave;

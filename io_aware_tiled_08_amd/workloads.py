@@ -346,3 +346,42 @@ def random_dout(B: int, H: int, N: int, d: int, dtype: str, seed: int) -> torch.
     random_qkv with tensor id 4."""
     return _draw(seed, TENSOR_DOUT, B, H, N, d, dtype,
                  lambda rng, b, h: rng.standard_normal((N, d), dtype=np.float32))
+
+
+@dataclasses.dataclass(frozen=True)
+class BwdWorkload:
+    """The backward pass on a square workload: gradients of Q, K, V."""
+
+    name: str
+    seed: int
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str
+    causal: bool
+    description: str = ""
+
+    @property
+    def scale(self) -> float:
+        return default_scale(self.d)
+
+    def flops(self) -> float:
+        """Algorithmic matrix-product FLOPs of the gradient: 2*N*N*d for each
+        of S = Q K^T, dV = P^T dO, dP = dO V^T, dQ = dS K and dK = dS^T Q per
+        head (2.5x the forward's count), halved under the causal mask.  The
+        kernels recompute S and dP once more (7 products instead of 5)."""
+        return 2.5 * metric_flops(self.B, self.H, self.N, self.d, self.causal)
+
+    def compulsory_bytes(self) -> int:
+        """Read Q, K, V, O, dO and LSE; write dQ, dK, dV (and D in and out)."""
+        e = ELEM_BYTES[self.dtype]
+        n = self.B * self.H * self.N
+        return 8 * n * self.d * e + 4 * n + 8 * n
+
+
+BWD_WORKLOADS = {
+    "headline_bwd_f16_d128": BwdWorkload(
+        "headline_bwd_f16_d128", 3, 2, 16, 4096, 128, "f16", False,
+        description="backward of B=2 H=16 N=4096 d=128 fp16, N(0,1) inputs and dO, non-causal"),
+}
