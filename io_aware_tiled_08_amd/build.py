@@ -18,7 +18,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libfa_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
-KERNEL_SOURCES = ("fa_fwd_f16.hip", "fa_fwd_f32.hip", "fa_fwd_kvcache.hip", "fa_fwd_fp8.hip", "fa_bwd.hip")
+KERNEL_SOURCES = ("fa_fwd_f16.hip", "fa_fwd_f16_ks.hip", "fa_fwd_f32.hip", "fa_fwd_kvcache.hip", "fa_fwd_fp8.hip", "fa_bwd.hip")
 
 
 def hipcc() -> str:

@@ -128,7 +128,8 @@ fa_status flash_attn_fwd(const void* q, const void* k, const void* v, void* o, f
   if (B > kLimit / H || N > kLimit / (B * H) || d * elem > kLimit / (B * H * N))
     return fail(FA_ERR_SHAPE, "B*H*N*d*elem overflows");
   const int64_t BH = B * H;
-  const int br = fa::rows_per_workgroup((fa::Dtype)dtype);
+  const bool keysplit = fa::use_keysplit((fa::Dtype)dtype, (int)d, causal != 0, BH, N);
+  const int br = keysplit ? fa::kRowsPerWorkgroupF16KeySplit : fa::rows_per_workgroup((fa::Dtype)dtype);
   const int64_t n_qblk = (N + br - 1) / br;
   const int64_t tpw = fa::threads_per_workgroup((fa::Dtype)dtype, (int)d);
   if (n_qblk > INT32_MAX || BH * n_qblk > (int64_t)UINT32_MAX / tpw)
@@ -160,6 +161,7 @@ fa_status flash_attn_fwd(const void* q, const void* k, const void* v, void* o, f
   a.dtype = (fa::Dtype)dtype;
   (void)hipGetLastError();  // do not report an earlier, unrelated error
   const hipError_t e = dtype == FA_F32 ? fa::launch_forward_f32(a, (hipStream_t)stream)
+                       : keysplit      ? fa::launch_forward_f16_keysplit(a, (hipStream_t)stream)
                                        : fa::launch_forward_f16(a, (hipStream_t)stream);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return FA_OK;

@@ -63,9 +63,14 @@ __device__ __forceinline__ constexpr int k_row_of_lane(int l32) {
 }
 
 // Workgroup -> (b*H + h, query block).  The dispatcher hands workgroup i to
-// XCD i % 8; the remap gives each XCD a contiguous range of blocks, so the
+// XCD i % 8; the remap gives each XCD a contiguous range of heads, so the
 // query blocks of one head share that XCD's L2 copy of the head's K and V.
-// Causal launches take the longest query blocks (highest index) first.
+// Causal launches take the longest query blocks (highest index) first.  With
+// at most four workgroups per CU (1024 in all) the order runs across the
+// XCD's heads (block-major, when its range holds whole heads), so that each
+// XCD starts all its longest blocks before any short one; longer launches
+// keep one head at a time per XCD (head-major), which keeps that head's K
+// and V hot in the XCD's L2.
 struct WorkItem {
   int64_t bh;
   int qblk;
@@ -74,8 +79,15 @@ template <bool CAUSAL>
 __device__ __forceinline__ WorkItem work_item(int n_qblk) {
   const int nblk = gridDim.x;
   const int wg = blockIdx.x;
-  const int logical = (nblk % 8 == 0) ? (wg % 8) * (nblk / 8) + wg / 8 : wg;
   WorkItem w;
+  if (CAUSAL && nblk <= 1024 && nblk % 8 == 0 && (nblk / 8) % n_qblk == 0) {
+    const int heads = nblk / 8 / n_qblk;  // heads per XCD
+    const int x = wg % 8, r = wg / 8;     // XCD, order within the XCD
+    w.bh = (int64_t)x * heads + r % heads;
+    w.qblk = n_qblk - 1 - r / heads;
+    return w;
+  }
+  const int logical = (nblk % 8 == 0) ? (wg % 8) * (nblk / 8) + wg / 8 : wg;
   w.bh = logical / n_qblk;
   w.qblk = logical % n_qblk;
   if (CAUSAL) w.qblk = n_qblk - 1 - w.qblk;

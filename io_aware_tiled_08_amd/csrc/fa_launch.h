@@ -26,6 +26,7 @@ struct FwdArgs {
 
 // Query rows owned by one workgroup (fixes the grid size).
 constexpr int kRowsPerWorkgroupF16 = 256;
+constexpr int kRowsPerWorkgroupF16KeySplit = 128;
 constexpr int kRowsPerWorkgroupF32 = 32;
 
 inline int rows_per_workgroup(Dtype dtype) {
@@ -41,5 +42,16 @@ inline int threads_per_workgroup(Dtype dtype, int d) {
 // Enqueue the forward kernel on `stream`; arguments are already validated.
 hipError_t launch_forward_f16(const FwdArgs& a, hipStream_t stream);  // FA_F16, FA_BF16
 hipError_t launch_forward_f32(const FwdArgs& a, hipStream_t stream);
+// Key-split schedule (d = 64 only): 128-row workgroups whose two wave groups
+// take alternate key tiles; for causal problems with few 256-row blocks.
+hipError_t launch_forward_f16_keysplit(const FwdArgs& a, hipStream_t stream);
+
+// Whether flash_attn_fwd uses the key-split schedule: causal, d = 64, and at
+// most two 256-row blocks per CU of the MI355X (256 CUs), where the
+// longest-first dispatch of 256-row blocks leaves CUs idle.
+inline bool use_keysplit(Dtype dtype, int d, bool causal, int64_t BH, int64_t N) {
+  return dtype != Dtype::F32 && d == 64 && causal &&
+         BH * ((N + kRowsPerWorkgroupF16 - 1) / kRowsPerWorkgroupF16) <= 2 * 256;
+}
 
 }  // namespace fa

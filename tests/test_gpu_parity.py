@@ -188,3 +188,17 @@ def test_workload_long_context():
     rows = W.sample_rows(w.seed, w.B, w.H, w.N, w.sampled_rows)
     check(o, lse, q, k, v, w.scale, w.causal, w.dtype, rows=rows, label=name)
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_causal_d64_many_blocks(dtype):
+    """Causal d=64 with more than 512 blocks of 256 rows (here 640): the
+    256-row schedule; the small causal d=64 cases above take the 128-row
+    key-split schedule."""
+    B, H, N, d = 8, 16, 1100, 64
+    q, k, v = W.random_qkv(B, H, N, d, dtype, seed=2100)
+    scale = W.default_scale(d)
+    o, lse = gpu_forward(q, k, v, scale, True)
+    rows = np.sort(np.concatenate([W.sample_rows(2100, B, H, N, 40),
+                                   np.broadcast_to(np.array([0, 255, 256, 1099]), (B, H, 4))], axis=2), axis=2)
+    check(o, lse, q, k, v, scale, True, dtype, rows=rows, label=f"{dtype} causal d=64 640 blocks")
