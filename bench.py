@@ -43,16 +43,16 @@ PEAK_CLOCK_MHZ = 2400.0  # the engine clock the published MFMA peaks are quoted 
 _CSRC = os.path.join(ROOT, "io_aware_tiled_08_amd", "csrc")
 # Source files each kernel is compiled from (its .hip and the headers it includes).
 KERNEL_SOURCES = {
-    "f16": ("fa_fwd_f16.hip", "fa_f16_common.h", "fa_device.h"),
-    "bf16": ("fa_fwd_f16.hip", "fa_f16_common.h", "fa_device.h"),
+    "f16": ("fa_fwd_f16.hip", "fa_fwd_f16_ks.hip", "fa_f16_common.h", "fa_device.h"),
+    "bf16": ("fa_fwd_f16.hip", "fa_fwd_f16_ks.hip", "fa_f16_common.h", "fa_device.h"),
     "f32": ("fa_fwd_f32.hip", "fa_device.h"),
     "kvcache": ("fa_fwd_kvcache.hip", "fa_f16_common.h", "fa_device.h"),
     "fp8": ("fa_fwd_fp8.hip", "fa_f16_common.h", "fa_device.h"),
     "bwd": ("fa_bwd.hip", "fa_f16_common.h", "fa_device.h"),
 }
 # (dominant kernel, every kernel of one call) name patterns in rocprofv3 output
-KERNEL_NAME_PATTERN = {"f16": ("fwd_f16_kernel", "fwd_f16_kernel"),
-                       "bf16": ("fwd_f16_kernel", "fwd_f16_kernel"),
+KERNEL_NAME_PATTERN = {"f16": ("fwd_f16_", "fwd_f16_"),
+                       "bf16": ("fwd_f16_", "fwd_f16_"),
                        "f32": ("fwd_f32_kernel", "fwd_f32_kernel"),
                        "kvcache": ("kvcache_fwd_kernel", "kvcache_"),
                        "fp8": ("fwd_fp8_kernel", "fwd_fp8_kernel"),
