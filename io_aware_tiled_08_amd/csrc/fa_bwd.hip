@@ -33,7 +33,8 @@
 namespace fa {
 namespace {
 
-constexpr int kBwdRows = 128;  // keys (dK/dV kernel) or queries (dQ kernel) per workgroup
+constexpr int kBwdRows = 128;  // keys per dK/dV workgroup (4 waves x 32)
+constexpr int kBwdWavesQ = 8;   // waves per dQ workgroup (32 queries each)
 constexpr int kBwdTile = 64;   // queries or keys per staged tile
 
 struct BwdParams {
@@ -48,7 +49,8 @@ struct BwdParams {
   void* dv;
   float* delta;  // workspace: D per row
   int64_t N;
-  int32_t n_blk;  // 128-row blocks per (b, h)
+  int32_t n_blk;    // 128-key blocks per (b, h) (dK/dV kernel)
+  int32_t n_blk_q;  // query blocks per (b, h) (dQ kernel)
   float c;        // scale * log2(e)
   float scale;
 };
@@ -106,13 +108,14 @@ struct TileOps {
   }
 };
 
-// Stage rows [r0, r0 + kBwdTile) of a [N, D] head into an LDS tile: the four
-// waves each issue kBwdTile*2D/1024/4 loads of 1 KiB; rows past N read zero.
-template <int D>
+// Stage rows [r0, r0 + kBwdTile) of a [N, D] head into an LDS tile: the NWL
+// waves each issue kBwdTile*2D/1024/NWL loads of 1 KiB; rows past N read zero.
+template <int D, int NWL>
 __device__ __forceinline__ void stage_tile(const void* head, int64_t r0, int64_t N, uint32_t lds,
                                            int wave, int lane) {
   constexpr int RB = 2 * D, CPR = D / 8, RPL = 1024 / RB;
-  constexpr int LPW = kBwdTile * RB / 1024 / 4;
+  constexpr int LPW = kBwdTile * RB / 1024 / NWL;
+  static_assert(LPW >= 1 && LPW * NWL * 1024 == kBwdTile * RB, "tile split");
   const uint32_t rows = (uint32_t)(N - r0 < kBwdTile ? N - r0 : kBwdTile);
   const u32x4 rs = buffer_rsrc((const char*)head + r0 * RB, rows * RB);
 #pragma unroll
@@ -204,8 +207,8 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p) {
     if (qt >= qt_end) return;
     const int buf = qt & 1;
     const int64_t r0 = (int64_t)qt * kBwdTile;
-    stage_tile<D>(Qh + r0 * D, 0, N - r0, lds_base + (buf * 2 + 0) * TILE, wave, lane);
-    stage_tile<D>(dOh + r0 * D, 0, N - r0, lds_base + (buf * 2 + 1) * TILE, wave, lane);
+    stage_tile<D, 4>(Qh + r0 * D, 0, N - r0, lds_base + (buf * 2 + 0) * TILE, wave, lane);
+    stage_tile<D, 4>(dOh + r0 * D, 0, N - r0, lds_base + (buf * 2 + 1) * TILE, wave, lane);
     if (wave == 0 && lane < 16) {  // 64 floats each: 16 lanes x 16 bytes
       const uint32_t rows = (uint32_t)(N - r0 < kBwdTile ? N - r0 : kBwdTile);
       dma_load16(buffer_rsrc(Lh + r0, rows * 4), stat_base + (buf * 2 + 0) * kBwdTile * 4, lane * 16);
@@ -330,7 +333,9 @@ __global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p) {
 
 // ---- dQ ----------------------------------------------------------------------
 template <typename T, int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, 1) bwd_dq_kernel(BwdParams p) {
+__global__ void __launch_bounds__(kBwdWavesQ * 64, 1) bwd_dq_kernel(BwdParams p) {
+  constexpr int NWQ = kBwdWavesQ;
+  constexpr int BRQ = 32 * NWQ;  // queries per workgroup
   using H = Half<T>;
   using Frag = typename H::Frag;
   using Pair = typename H::Pair;
@@ -347,10 +352,10 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(BwdParams p) {
   const int l32 = lane & 31, hh = lane >> 5;
   // XCD-aware order; causal: the longest query blocks (highest index) first.
   const int logical = xcd_order();
-  const int64_t bh = logical / p.n_blk;
-  int qblk = logical % p.n_blk;
-  if (CAUSAL) qblk = p.n_blk - 1 - qblk;
-  const int64_t q0 = (int64_t)qblk * kBwdRows;
+  const int64_t bh = logical / p.n_blk_q;
+  int qblk = logical % p.n_blk_q;
+  if (CAUSAL) qblk = p.n_blk_q - 1 - qblk;
+  const int64_t q0 = (int64_t)qblk * BRQ;
   const int64_t qw = q0 + 32 * wave;
   const int64_t qrow = qw + l32;
 
@@ -377,7 +382,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(BwdParams p) {
     }
   }
 
-  const int64_t kv_end = CAUSAL ? (q0 + kBwdRows < N ? q0 + kBwdRows : N) : N;
+  const int64_t kv_end = CAUSAL ? (q0 + BRQ < N ? q0 + BRQ : N) : N;
   const int n_tiles = (int)((kv_end + kBwdTile - 1) / kBwdTile);
   const int64_t wave_end = CAUSAL ? (qw + 32 < N ? qw + 32 : N) : N;
   const int wave_tiles = qw < N ? (int)((wave_end + kBwdTile - 1) / kBwdTile) : 0;
@@ -386,8 +391,8 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(BwdParams p) {
     if (t >= n_tiles) return;
     const int buf = t & 1;
     const int64_t r0 = (int64_t)t * kBwdTile;
-    stage_tile<D>(Kh + r0 * D, 0, N - r0, lds_base + (buf * 2 + 0) * TILE, wave, lane);
-    stage_tile<D>(Vh + r0 * D, 0, N - r0, lds_base + (buf * 2 + 1) * TILE, wave, lane);
+    stage_tile<D, NWQ>(Kh + r0 * D, 0, N - r0, lds_base + (buf * 2 + 0) * TILE, wave, lane);
+    stage_tile<D, NWQ>(Vh + r0 * D, 0, N - r0, lds_base + (buf * 2 + 1) * TILE, wave, lane);
   };
 
   f32x16 dq[ND];
@@ -405,7 +410,7 @@ __global__ void __launch_bounds__(256, 1) bwd_dq_kernel(BwdParams p) {
   }
   fence(lse2);
   fence(drow);
-  constexpr int LPW = TILE / 1024 / 4;
+  constexpr int LPW = TILE / 1024 / NWQ;
   for (int t = 0; t < n_tiles; ++t) {
     if (t + 1 < n_tiles) {
       issue(t + 1);
@@ -487,6 +492,7 @@ hipError_t launch(const BwdArgs& a, hipStream_t stream) {
   p.delta = (float*)a.workspace;
   p.N = a.N;
   p.n_blk = (int32_t)((a.N + kBwdRows - 1) / kBwdRows);
+  p.n_blk_q = (int32_t)((a.N + 32 * kBwdWavesQ - 1) / (32 * kBwdWavesQ));
   p.c = a.scale * kLog2e;
   p.scale = a.scale;
   const int64_t rows = a.BH * a.N;
@@ -499,7 +505,8 @@ hipError_t launch(const BwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3(grid), dim3(256), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3(grid), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3((unsigned)(a.BH * p.n_blk_q)),
+                     dim3(kBwdWavesQ * 64), 0, stream, p);
   return hipGetLastError();
 }
 
