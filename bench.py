@@ -390,6 +390,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, run device copies of a known size "
                          "(for calibrating rocprofv3 FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--persistent", type=int, default=None, metavar="NWG",
+                    help="run an fp16/bf16 forward workload on the persistent schedule with NWG "
+                         "resident workgroups (0 = one per CU)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic_<workload>.md from two rocprofv3 --pmc runs")
     args = ap.parse_args()
@@ -406,6 +409,8 @@ def main():
         sys.exit(2)
     w, key = workload_by_name(name)
     cache = key == "kvcache"
+    if args.persistent is not None and key not in ("f16", "bf16"):
+        raise SystemExit("--persistent applies to the fp16/bf16 forward workloads")
 
     import torch
 
@@ -451,6 +456,16 @@ def main():
         def step():
             flash_attn_fwd_fp8(qd, kd, vd, o, lse, q_descale=qs, k_descale=ks, v_descale=vs,
                                scale=w.scale, causal=w.causal, stream=stream)
+    elif args.persistent is not None:
+        from io_aware_tiled_08_amd import flash_attn_fwd_persistent
+        q, k, v = W.workload_inputs(w)
+        qd, kd, vd = (x.to(dev) for x in (q, k, v))
+        o = torch.empty_like(qd)
+        lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+
+        def step():
+            flash_attn_fwd_persistent(qd, kd, vd, o, lse, scale=w.scale, causal=w.causal,
+                                      num_workgroups=args.persistent, stream=stream)
     else:
         q, k, v = W.workload_inputs(w)
         qd, kd, vd = (x.to(dev) for x in (q, k, v))
@@ -513,7 +528,8 @@ def main():
     tflops = flops / (ms * 1e-3) / 1e12
     comp = w.compulsory_bytes()
     gbps = comp / (ms * 1e-3) / 1e9
-    traffic = measured_traffic(name, key)
+    # Stored counters describe the default schedule's kernel.
+    traffic = measured_traffic(name, key) if args.persistent is None else None
     dist = [round(percentile(per_launch, f), 5) for f in (0.1, 0.5, 0.9)]
     props = torch.cuda.get_device_properties(dev)
     mhz = clock.median_mhz()
@@ -593,6 +609,9 @@ def main():
                        "causal": w.causal, "inputs": w.description},
             "roofline": roofline,
         }
+        if args.persistent is not None:
+            result["config"]["schedule"] = "persistent"
+            result["config"]["num_workgroups"] = args.persistent
     result["device"] = {"name": props.name, "cus": props.multi_processor_count,
                         "arch": getattr(props, "gcnArchName", "")}
     result["timed_wall_s"] = round(wall, 4)

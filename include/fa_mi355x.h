@@ -28,7 +28,7 @@
 extern "C" {
 #endif
 
-#define FA_MI355X_ABI_VERSION 4
+#define FA_MI355X_ABI_VERSION 5
 
 typedef enum {
   FA_F32 = 0,   /* IEEE binary32 */
@@ -101,6 +101,36 @@ fa_status flash_attn_fwd(const void* q, const void* k, const void* v,
                          int64_t B, int64_t H, int64_t N, int64_t d,
                          float scale, int causal,
                          fa_dtype dtype, void* stream);
+
+/*
+ * flash_attn_fwd_persistent -- flash_attn_fwd's computation (fp16 and bf16)
+ * under a persistent schedule.
+ *
+ * Source: "FlashAttention" (Chapter 15, vizuara), "FlashAttention Evolution",
+ * FA-4 card (persistent kernels); the computation is flash_attn_fwd's (same
+ * pages).  Instead of one workgroup per 256-row query block, a fixed grid of
+ * num_workgroups workgroups stays resident and each loops over the blocks:
+ * causal blocks longest first, dealt to the workgroups in a snake order
+ * (workgroup g takes block r*G + g in even rounds and r*G + G-1-g in odd
+ * ones, G the grid size); unmasked blocks head-major, a contiguous range of
+ * them per XCD and round.  Each block is computed exactly as flash_attn_fwd's
+ * 256-row kernel computes it, so o and lse are bitwise equal to that
+ * kernel's (flash_attn_fwd itself takes another schedule for causal d = 64
+ * problems with few blocks, whose rounding can differ in the last bit).
+ *
+ * Arguments as for flash_attn_fwd, plus
+ *   num_workgroups  resident workgroups; 0 = one per compute unit of the
+ *                   current device.  Clamped to the number of blocks,
+ *                   B * H * ceil(N / 256).
+ * dtype must be FA_F16 or FA_BF16 (FA_F32 returns FA_ERR_DTYPE).
+ *
+ * Errors as for flash_attn_fwd, plus FA_ERR_SHAPE for num_workgroups < 0.
+ */
+fa_status flash_attn_fwd_persistent(const void* q, const void* k, const void* v,
+                                    void* o, float* lse,
+                                    int64_t B, int64_t H, int64_t N, int64_t d,
+                                    float scale, int causal, int num_workgroups,
+                                    fa_dtype dtype, void* stream);
 
 /*
  * flash_attn_fwd_kvcache -- attention of Nq new queries against a key/value

@@ -23,10 +23,10 @@ STATUS = {
     8: "FA_ERR_NO_DEVICE", 9: "FA_ERR_ARCH", 10: "FA_ERR_HIP", 11: "FA_ERR_WORKSPACE",
 }
 STATUS_CODE = {name: code for code, name in STATUS.items()}
-EXPORTS = ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_workspace_size", "flash_attn_fwd_fp8", "flash_attn_fwd_kvcache", "flash_attn_kvcache_splits",
+EXPORTS = ("flash_attn_fwd", "flash_attn_fwd_persistent", "flash_attn_bwd", "flash_attn_bwd_workspace_size", "flash_attn_fwd_fp8", "flash_attn_fwd_kvcache", "flash_attn_kvcache_splits",
            "flash_attn_kvcache_workspace_size", "flash_attn_status_str",
            "flash_attn_last_error", "flash_attn_abi_version")
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 _lib = None
 _lock = threading.Lock()
@@ -57,6 +57,9 @@ def lib() -> ctypes.CDLL:
             L.flash_attn_fwd.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 4 + [
                 ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
             L.flash_attn_fwd.restype = ctypes.c_int
+            L.flash_attn_fwd_persistent.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64] * 4 + [
+                ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+            L.flash_attn_fwd_persistent.restype = ctypes.c_int
             L.flash_attn_bwd.argtypes = [ctypes.c_void_p] * 9 + [ctypes.c_int64] * 4 + [
                 ctypes.c_float, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
                 ctypes.c_void_p]
@@ -108,17 +111,8 @@ def _dtype_code(t) -> int:
     return codes[t.dtype]
 
 
-def flash_attn_fwd(q, k, v, o=None, lse=None, *, scale: Optional[float] = None,
-                   causal: bool = False, stream=None) -> Tuple["object", "object"]:
-    """O = softmax(scale * Q K^T) V and LSE for contiguous [B, H, N, d] tensors.
-
-    q, k, v: device tensors of one dtype (float32, float16 or bfloat16).
-    o, lse: optional preallocated outputs ([B, H, N, d] of q's dtype and
-    [B, H, N] float32); allocated here when omitted.
-    scale: defaults to 1/sqrt(d).  causal: lower-triangular mask (j <= i).
-    stream: a torch.cuda.Stream; defaults to the current stream of q's device.
-    The kernel is enqueued asynchronously on that stream.
-    """
+def _forward_operands(q, k, v, o, lse, scale):
+    """Check q, k, v (and o, lse when given), allocate missing outputs."""
     import torch
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
@@ -144,15 +138,58 @@ def flash_attn_fwd(q, k, v, o=None, lse=None, *, scale: Optional[float] = None,
     if (lse.shape != (B, H, N) or lse.dtype != torch.float32 or lse.device != q.device
             or not lse.is_contiguous()):
         raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    return (B, H, N, d), code, float(scale), o, lse
+
+
+def flash_attn_fwd(q, k, v, o=None, lse=None, *, scale: Optional[float] = None,
+                   causal: bool = False, stream=None) -> Tuple["object", "object"]:
+    """O = softmax(scale * Q K^T) V and LSE for contiguous [B, H, N, d] tensors.
+
+    q, k, v: device tensors of one dtype (float32, float16 or bfloat16).
+    o, lse: optional preallocated outputs ([B, H, N, d] of q's dtype and
+    [B, H, N] float32); allocated here when omitted.
+    scale: defaults to 1/sqrt(d).  causal: lower-triangular mask (j <= i).
+    stream: a torch.cuda.Stream; defaults to the current stream of q's device.
+    The kernel is enqueued asynchronously on that stream.
+    """
+    import torch
+    (B, H, N, d), code, scale, o, lse = _forward_operands(q, k, v, o, lse, scale)
     L = lib()
     with torch.cuda.device(q.device):
         s = stream if stream is not None else torch.cuda.current_stream(q.device)
         st = L.flash_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                              lse.data_ptr(), B, H, N, d, float(scale), int(bool(causal)),
+                              lse.data_ptr(), B, H, N, d, scale, int(bool(causal)),
                               code, s.cuda_stream)
     if st != 0:
         raise FlashAttnError(st, L.flash_attn_last_error().decode())
     return o, lse
+
+
+def flash_attn_fwd_persistent(q, k, v, o=None, lse=None, *, scale: Optional[float] = None,
+                              causal: bool = False, num_workgroups: int = 0,
+                              stream=None) -> Tuple["object", "object"]:
+    """flash_attn_fwd (float16 / bfloat16) on a persistent grid of
+    num_workgroups resident workgroups (0: one per compute unit) that loop
+    over the 256-row query blocks.  Arguments otherwise as flash_attn_fwd."""
+    import torch
+    (B, H, N, d), code, scale, o, lse = _forward_operands(q, k, v, o, lse, scale)
+    L = lib()
+    with torch.cuda.device(q.device):
+        s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        st = L.flash_attn_fwd_persistent(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                         lse.data_ptr(), B, H, N, d, scale, int(bool(causal)),
+                                         int(num_workgroups), code, s.cuda_stream)
+    if st != 0:
+        raise FlashAttnError(st, L.flash_attn_last_error().decode())
+    return o, lse
+
+
+def flash_attn_fwd_persistent_ptr(q: int, k: int, v: int, o: int, lse: int, B: int, H: int,
+                                  N: int, d: int, scale: float, causal: bool,
+                                  num_workgroups: int, dtype: int, stream: int = 0) -> int:
+    """Raw call of the C entry point on integer addresses; returns the status."""
+    return lib().flash_attn_fwd_persistent(q, k, v, o, lse, B, H, N, d, scale,
+                                           int(bool(causal)), num_workgroups, dtype, stream)
 
 
 def kvcache_splits(B: int, H: int, Nq: int, Nk: int, d: int, num_splits: int = 0) -> int:

@@ -40,6 +40,7 @@ bool overlaps(const void* a, int64_t a_bytes, const void* b, int64_t b_bytes) {
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch_ok[kMaxDevices];
 char g_arch_name[kMaxDevices][64];
+int g_cu_count[kMaxDevices];  // compute units, valid once g_arch_ok[dev] != 0
 
 fa_status check_device() {
   int dev = -1;
@@ -55,6 +56,7 @@ fa_status check_device() {
       return fail(FA_ERR_NO_DEVICE, "hipGetDeviceProperties(%d): %s", dev, hipGetErrorString(e));
     // gcnArchName looks like "gfx950:sramecc+:xnack-".
     std::snprintf(g_arch_name[dev], sizeof(g_arch_name[dev]), "%s", prop.gcnArchName);
+    g_cu_count[dev] = prop.multiProcessorCount;
     state = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 &&
                     (prop.gcnArchName[6] == '\0' || prop.gcnArchName[6] == ':')
                 ? 1
@@ -101,20 +103,22 @@ int64_t kv_workspace_bytes(int64_t BH, int64_t Nq, int64_t d, int n_split) {
   return n_split > 1 ? (int64_t)n_split * BH * Nq * (d + 1) * 4 : 0;
 }
 
-}  // namespace
-
-extern "C" {
-
-fa_status flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                         int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
-                         fa_dtype dtype, void* stream) {
-  g_last_error[0] = '\0';
+// Argument checks of flash_attn_fwd and flash_attn_fwd_persistent (the latter
+// always uses 256-row blocks): FA_OK with *a filled and *empty false when a
+// kernel is to be launched, FA_OK with *empty true for an empty problem.
+fa_status check_forward(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
+                        fa_dtype dtype, bool persistent, fa::FwdArgs* a, bool* keysplit,
+                        bool* empty) {
+  *empty = true;
   if (B < 0 || H < 0 || N < 0)
     return fail(FA_ERR_SHAPE, "B, H, N must be >= 0 (got %lld, %lld, %lld)", (long long)B,
                 (long long)H, (long long)N);
   if (d != 64 && d != 128) return fail(FA_ERR_HEAD_DIM, "d must be 64 or 128 (got %lld)", (long long)d);
   if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16)
     return fail(FA_ERR_DTYPE, "unknown dtype %d", (int)dtype);
+  if (persistent && dtype == FA_F32)
+    return fail(FA_ERR_DTYPE, "the persistent schedule runs fp16 and bf16 only");
   if (!std::isfinite(scale)) return fail(FA_ERR_SCALE, "scale must be finite");
   // An empty problem reads no pointer (zero-size buffers may be NULL).
   if (B == 0 || H == 0 || N == 0) return FA_OK;
@@ -128,8 +132,8 @@ fa_status flash_attn_fwd(const void* q, const void* k, const void* v, void* o, f
   if (B > kLimit / H || N > kLimit / (B * H) || d * elem > kLimit / (B * H * N))
     return fail(FA_ERR_SHAPE, "B*H*N*d*elem overflows");
   const int64_t BH = B * H;
-  const bool keysplit = fa::use_keysplit((fa::Dtype)dtype, (int)d, causal != 0, BH, N);
-  const int br = keysplit ? fa::kRowsPerWorkgroupF16KeySplit : fa::rows_per_workgroup((fa::Dtype)dtype);
+  *keysplit = !persistent && fa::use_keysplit((fa::Dtype)dtype, (int)d, causal != 0, BH, N);
+  const int br = *keysplit ? fa::kRowsPerWorkgroupF16KeySplit : fa::rows_per_workgroup((fa::Dtype)dtype);
   const int64_t n_qblk = (N + br - 1) / br;
   const int64_t tpw = fa::threads_per_workgroup((fa::Dtype)dtype, (int)d);
   if (n_qblk > INT32_MAX || BH * n_qblk > (int64_t)UINT32_MAX / tpw)
@@ -144,25 +148,66 @@ fa_status flash_attn_fwd(const void* q, const void* k, const void* v, void* o, f
       overlaps(lse, lbytes, o, tbytes))
     return fail(FA_ERR_ALIAS, "o and lse must not overlap q, k, v or each other");
 
-  fa_status st = check_device();
-  if (st != FA_OK) return st;
+  a->q = q;
+  a->k = k;
+  a->v = v;
+  a->o = o;
+  a->lse = lse;
+  a->BH = BH;
+  a->N = N;
+  a->d = (int)d;
+  a->scale = scale;
+  a->causal = causal != 0;
+  a->dtype = (fa::Dtype)dtype;
+  *empty = false;
+  return FA_OK;
+}
 
+}  // namespace
+
+extern "C" {
+
+fa_status flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int64_t B, int64_t H, int64_t N, int64_t d, float scale, int causal,
+                         fa_dtype dtype, void* stream) {
+  g_last_error[0] = '\0';
   fa::FwdArgs a;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.o = o;
-  a.lse = lse;
-  a.BH = BH;
-  a.N = N;
-  a.d = (int)d;
-  a.scale = scale;
-  a.causal = causal != 0;
-  a.dtype = (fa::Dtype)dtype;
+  bool keysplit = false, empty = true;
+  fa_status st = check_forward(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, false, &a,
+                               &keysplit, &empty);
+  if (st != FA_OK || empty) return st;
+  st = check_device();
+  if (st != FA_OK) return st;
   (void)hipGetLastError();  // do not report an earlier, unrelated error
   const hipError_t e = dtype == FA_F32 ? fa::launch_forward_f32(a, (hipStream_t)stream)
                        : keysplit      ? fa::launch_forward_f16_keysplit(a, (hipStream_t)stream)
                                        : fa::launch_forward_f16(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
+fa_status flash_attn_fwd_persistent(const void* q, const void* k, const void* v, void* o,
+                                    float* lse, int64_t B, int64_t H, int64_t N, int64_t d,
+                                    float scale, int causal, int num_workgroups, fa_dtype dtype,
+                                    void* stream) {
+  g_last_error[0] = '\0';
+  if (num_workgroups < 0)
+    return fail(FA_ERR_SHAPE, "num_workgroups must be >= 0 (got %d)", num_workgroups);
+  fa::FwdArgs a;
+  bool keysplit = false, empty = true;
+  fa_status st = check_forward(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, true, &a,
+                               &keysplit, &empty);
+  if (st != FA_OK || empty) return st;
+  st = check_device();
+  if (st != FA_OK) return st;
+  int dev = 0;
+  (void)hipGetDevice(&dev);  // succeeded inside check_device
+  const int64_t items = a.BH * ((N + fa::kRowsPerWorkgroupF16 - 1) / fa::kRowsPerWorkgroupF16);
+  int64_t n_wg = num_workgroups > 0 ? num_workgroups : g_cu_count[dev];
+  if (n_wg < 1) n_wg = 1;
+  if (n_wg > items) n_wg = items;
+  (void)hipGetLastError();
+  const hipError_t e = fa::launch_forward_f16_persistent(a, (int)n_wg, (hipStream_t)stream);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return FA_OK;
 }

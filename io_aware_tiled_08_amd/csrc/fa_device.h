@@ -28,6 +28,7 @@ struct KernelParams {
   int32_t n_qblk;   // query blocks per (b, h)
   float c;          // |scale| * log2(e): scores are kept in log2 units
   uint32_t q_sign;  // XOR mask on Q's bits: flips Q's sign when scale < 0
+  int64_t n_items;  // B * H * n_qblk (the persistent schedule's item count)
 };
 
 template <typename To, typename From>

@@ -52,8 +52,13 @@
 namespace fa {
 namespace {
 
+// One 256-row query block (work item wi) of one (batch, head): the whole
+// pass from the Q load to the O and LSE stores.  Every wave of the workgroup
+// calls it with the same wi; on return all LDS reads of the item are done
+// (the last statement before the stores is a workgroup barrier), so a
+// workgroup may call it again for its next item.
 template <typename T, int D, bool CAUSAL>
-__global__ void __launch_bounds__(512, 1) fwd_f16_kernel(KernelParams p) {
+__device__ __forceinline__ void fwd_f16_block(const KernelParams& p, const WorkItem wi) {
   using H = Half<T>;
   using Frag = typename H::Frag;
   using Pair = typename H::Pair;
@@ -73,7 +78,6 @@ __global__ void __launch_bounds__(512, 1) fwd_f16_kernel(KernelParams p) {
 
   __shared__ __attribute__((aligned(1024))) char smem[2][2][TILE];  // [K, V][buffer]
 
-  const WorkItem wi = work_item<CAUSAL>(p.n_qblk);
   const int64_t N = p.N;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -381,8 +385,45 @@ __global__ void __launch_bounds__(512, 1) fwd_f16_kernel(KernelParams p) {
   }
 }
 
+// One workgroup per 256-row block; the hardware dispatcher hands the blocks
+// to CUs in the order of work_item (longest first when causal).
 template <typename T, int D, bool CAUSAL>
-hipError_t launch(const FwdArgs& a, hipStream_t stream) {
+__global__ void __launch_bounds__(512, 1) fwd_f16_kernel(KernelParams p) {
+  fwd_f16_block<T, D, CAUSAL>(p, work_item<CAUSAL>(p.n_qblk));
+}
+
+// Persistent schedule ("FlashAttention Evolution", FA-4 card: persistent
+// kernels): a grid of G resident workgroups, each looping over the work items
+// in rounds of G.  Causal items are ordered longest first (block-major across
+// heads) and dealt in a snake: workgroup g takes item r*G + g in even rounds
+// and r*G + G-1-g in odd ones, so over two rounds every workgroup gets about
+// the same number of tiles.  When G and B*H are multiples of 8, the items of
+// a workgroup all share one residue of (b*H + h) mod 8 per round parity, so
+// an XCD (workgroup g runs on XCD g % 8) keeps to a few heads.  Unmasked items
+// are equal in cost: workgroup g of XCD x takes a contiguous range of items
+// per round, head-major, so a head's blocks share that XCD's L2.
+template <typename T, int D, bool CAUSAL>
+__global__ void __launch_bounds__(512, 1) fwd_f16_persistent_kernel(KernelParams p) {
+  const int G = gridDim.x, g = blockIdx.x;
+  const int gx = (!CAUSAL && G % 8 == 0) ? (g % 8) * (G / 8) + g / 8 : g;
+  const int64_t n_bh = p.n_items / p.n_qblk;
+  for (int64_t r = 0;; ++r) {
+    const int64_t j = r * G + ((CAUSAL && (r & 1)) ? G - 1 - gx : gx);
+    if (j >= p.n_items) break;
+    WorkItem wi;
+    if (CAUSAL) {
+      wi.bh = j % n_bh;
+      wi.qblk = p.n_qblk - 1 - (int)(j / n_bh);
+    } else {
+      wi.bh = j / p.n_qblk;
+      wi.qblk = (int)(j % p.n_qblk);
+    }
+    fwd_f16_block<T, D, CAUSAL>(p, wi);
+  }
+}
+
+template <typename T, int D, bool CAUSAL>
+KernelParams make_params(const FwdArgs& a) {
   constexpr int BR = 256;
   static_assert(BR == kRowsPerWorkgroupF16, "rows per workgroup");
   KernelParams p;
@@ -398,21 +439,39 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   // exp2(0) = 1.
   p.c = __builtin_fmaxf(__builtin_fabsf(a.scale) * kLog2e, 1.17549435e-38f);
   p.q_sign = a.scale < 0.f ? 0x80008000u : 0u;
-  hipLaunchKernelGGL((fwd_f16_kernel<T, D, CAUSAL>), dim3((unsigned)(a.BH * p.n_qblk)), dim3(512),
-                     0, stream, p);
+  p.n_items = a.BH * p.n_qblk;
+  return p;
+}
+
+// n_wg == 0: one workgroup per block; else the persistent kernel on n_wg
+// workgroups (1 <= n_wg <= blocks).
+template <typename T, int D, bool CAUSAL>
+hipError_t launch(const FwdArgs& a, int n_wg, hipStream_t stream) {
+  const KernelParams p = make_params<T, D, CAUSAL>(a);
+  if (n_wg == 0)
+    hipLaunchKernelGGL((fwd_f16_kernel<T, D, CAUSAL>), dim3((unsigned)p.n_items), dim3(512), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL((fwd_f16_persistent_kernel<T, D, CAUSAL>), dim3((unsigned)n_wg), dim3(512),
+                       0, stream, p);
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
-  if (a.d == 64) return a.causal ? launch<T, 64, true>(a, s) : launch<T, 64, false>(a, s);
-  return a.causal ? launch<T, 128, true>(a, s) : launch<T, 128, false>(a, s);
+hipError_t launch_t(const FwdArgs& a, int n_wg, hipStream_t s) {
+  if (a.d == 64) return a.causal ? launch<T, 64, true>(a, n_wg, s) : launch<T, 64, false>(a, n_wg, s);
+  return a.causal ? launch<T, 128, true>(a, n_wg, s) : launch<T, 128, false>(a, n_wg, s);
 }
 
 }  // namespace
 
 hipError_t launch_forward_f16(const FwdArgs& a, hipStream_t stream) {
-  return a.dtype == Dtype::BF16 ? launch_t<__bf16>(a, stream) : launch_t<_Float16>(a, stream);
+  return a.dtype == Dtype::BF16 ? launch_t<__bf16>(a, 0, stream) : launch_t<_Float16>(a, 0, stream);
+}
+
+hipError_t launch_forward_f16_persistent(const FwdArgs& a, int n_wg, hipStream_t stream) {
+  return a.dtype == Dtype::BF16 ? launch_t<__bf16>(a, n_wg, stream)
+                                : launch_t<_Float16>(a, n_wg, stream);
 }
 
 }  // namespace fa

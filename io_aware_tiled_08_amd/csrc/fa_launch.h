@@ -42,6 +42,9 @@ inline int threads_per_workgroup(Dtype dtype, int d) {
 // Enqueue the forward kernel on `stream`; arguments are already validated.
 hipError_t launch_forward_f16(const FwdArgs& a, hipStream_t stream);  // FA_F16, FA_BF16
 hipError_t launch_forward_f32(const FwdArgs& a, hipStream_t stream);
+// Persistent schedule: n_wg workgroups (1 <= n_wg <= B*H*ceil(N/256)) loop
+// over the 256-row blocks (FA_F16, FA_BF16).
+hipError_t launch_forward_f16_persistent(const FwdArgs& a, int n_wg, hipStream_t stream);
 // Key-split schedule (d = 64 only): 128-row workgroups whose two wave groups
 // take alternate key tiles; for causal problems with few 256-row blocks.
 hipError_t launch_forward_f16_keysplit(const FwdArgs& a, hipStream_t stream);

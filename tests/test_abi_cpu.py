@@ -308,3 +308,38 @@ def test_fp8_no_device_reported_not_crashed(L):
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert _f8(L)[0] == 8
+
+
+# ---- persistent schedule -----------------------------------------------------
+def _pers(L, q=Q, k=K, v=V, o=O, lse=LSE, B=2, H=3, N=100, d=64, scale=0.125, causal=0,
+          nwg=0, dtype=1):
+    st = L.flash_attn_fwd_persistent(q, k, v, o, lse, B, H, N, d, scale, causal, nwg, dtype, None)
+    return st, L.flash_attn_last_error().decode()
+
+
+def test_persistent_argument_checks_match_the_forward(L):
+    """Same checks, same codes as flash_attn_fwd, before any HIP call."""
+    for kw in ({"q": None}, {"lse": None}, {"B": -1}, {"d": 96}, {"dtype": 7}, {"v": V + 8},
+               {"scale": math.nan}, {"o": K}, {"B": 1 << 40, "H": 1 << 20, "N": 1 << 10},
+               {"B": 1 << 20, "H": 1 << 11, "N": 1 << 10}):
+        assert _pers(L, **kw)[0] == _call(L, **kw)[0] != 0, kw
+
+
+def test_persistent_rejects_fp32_and_negative_grid(L):
+    st, msg = _pers(L, dtype=0)
+    assert st == 4 and "fp16 and bf16" in msg
+    st, msg = _pers(L, nwg=-1)
+    assert st == 2 and "num_workgroups" in msg
+
+
+def test_persistent_empty_is_a_no_op(L):
+    assert _pers(L, N=0, q=None, o=None, lse=None) == (0, "")
+    assert _pers(L, B=0, nwg=5) == (0, "")
+
+
+def test_persistent_no_device_reported_not_crashed(L):
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _pers(L)[0] == 8
+    assert _pers(L, nwg=3, causal=1)[0] == 8
