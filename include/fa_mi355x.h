@@ -28,7 +28,7 @@
 extern "C" {
 #endif
 
-#define FA_MI355X_ABI_VERSION 5
+#define FA_MI355X_ABI_VERSION 6
 
 typedef enum {
   FA_F32 = 0,   /* IEEE binary32 */
@@ -234,7 +234,8 @@ fa_status flash_attn_fwd_fp8(const void* q, const void* k, const void* v,
  * them (same scale and causal); dq, dk, dv contiguous [B, H, N, d] of
  * `dtype`, fully overwritten; workspace: device scratch owned by the caller,
  * 16-byte aligned, at least flash_attn_bwd_workspace_size(B, H, N) bytes (it
- * receives D; its contents on entry do not matter).  B, H, N, d, scale,
+ * receives D and lse * log2(e) per row; its contents on entry do not
+ * matter).  B, H, N, d, scale,
  * causal, stream as for flash_attn_fwd.  P and dS are rounded to `dtype`
  * before the products that use them (accuracy contract: the per-element
  * bound derived from those roundings and from o's).  Enqueues three kernels
@@ -250,7 +251,7 @@ fa_status flash_attn_bwd(const void* q, const void* k, const void* v,
                          void* workspace, int64_t workspace_bytes,
                          fa_dtype dtype, void* stream);
 
-/* Workspace bytes flash_attn_bwd needs: B * H * N * 4 (0 for empty sizes, -1
+/* Workspace bytes flash_attn_bwd needs: B * H * N * 8 (0 for empty sizes, -1
  * if that overflows).  No HIP call. */
 int64_t flash_attn_bwd_workspace_size(int64_t B, int64_t H, int64_t N);
 

@@ -26,7 +26,7 @@ STATUS_CODE = {name: code for code, name in STATUS.items()}
 EXPORTS = ("flash_attn_fwd", "flash_attn_fwd_persistent", "flash_attn_bwd", "flash_attn_bwd_workspace_size", "flash_attn_fwd_fp8", "flash_attn_fwd_kvcache", "flash_attn_kvcache_splits",
            "flash_attn_kvcache_workspace_size", "flash_attn_status_str",
            "flash_attn_last_error", "flash_attn_abi_version")
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 _lib = None
 _lock = threading.Lock()

@@ -271,7 +271,7 @@ fa_status flash_attn_fwd_fp8(const void* q, const void* k, const void* v, void* 
 int64_t flash_attn_bwd_workspace_size(int64_t B, int64_t H, int64_t N) {
   if (B <= 0 || H <= 0 || N <= 0) return 0;
   if (B > ((int64_t)1 << 40) / H || N > ((int64_t)1 << 40) / (B * H)) return -1;
-  return B * H * N * 4;
+  return B * H * N * 8;
 }
 
 fa_status flash_attn_bwd(const void* q, const void* k, const void* v, const void* o,

@@ -19,7 +19,7 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  void* workspace;  // B * H * N floats (D = rowsum(dO * O))
+  void* workspace;  // 2 * B * H * N floats: D = rowsum(dO * O), then LSE * log2(e)
   int64_t BH;
   int64_t N;
   int d;
@@ -29,7 +29,7 @@ struct BwdArgs {
 };
 
 constexpr int kBwdRowsPerWorkgroup = 128;
-constexpr int kBwdThreads = 256;
+constexpr int kBwdThreads = 512;
 
 hipError_t launch_backward(const BwdArgs& a, hipStream_t stream);  // FA_F16, FA_BF16
 

@@ -26,6 +26,8 @@
 // Every tile is read both by rows (MFMA A operands) and transposed
 // (ds_read_b64_tr_b16, for the d x rows operands); one XOR permutation of the
 // 16-byte chunks of a row serves both without LDS bank conflicts.
+#include <type_traits>
+
 #include "fa_bwd.h"
 #include "fa_device.h"
 #include "fa_f16_common.h"
@@ -48,6 +50,7 @@ struct BwdParams {
   void* dk;
   void* dv;
   float* delta;  // workspace: D per row
+  float* lse2;   // workspace: LSE * log2(e) per row
   int64_t N;
   int32_t n_blk;    // 128-key blocks per (b, h) (dK/dV kernel)
   int32_t n_blk_q;  // query blocks per (b, h) (dQ kernel)
@@ -83,7 +86,10 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams p, int64_t rows
   }
 #pragma unroll
   for (int w = TPR / 2; w > 0; w >>= 1) acc += __shfl_xor(acc, w, TPR);
-  if (row < rows && c8 == 0) p.delta[row] = acc;
+  if (row < rows && c8 == 0) {
+    p.delta[row] = acc;
+    p.lse2[row] = p.lse[row] * kLog2e;
+  }
 }
 
 // Row-read and transposing-read helpers over a staged [kBwdTile x D] tile.
@@ -152,181 +158,295 @@ __device__ __forceinline__ void block_barrier() {
 }
 
 // ---- dK, dV ------------------------------------------------------------------
+// A workgroup owns 128 keys in four groups of 32 and runs eight waves: wave g
+// (g < 4, "P wave") and wave g + 4 ("dS wave") share key group g and a SIMD.
+// For each 32-query tile the P wave computes S = Q K^T (K in registers),
+// P = exp2(c S - LSE log2 e) and dV^T += dO^T P; the dS wave computes
+// dP = dO V^T (V in registers), takes P from its partner through LDS, and
+// accumulates dK^T += Q^T dS with dS = P (dP - D).  One workgroup barrier per
+// tile separates "P written" from "P read"; while one wave of a SIMD runs its
+// vector work the other issues matrix products.  Q/dO tiles and their LSE and
+// D rows are loaded into LDS kDkvBufs - 1 tiles ahead.
+constexpr int kDkvQ = 32;    // queries per staged tile
+constexpr int kDkvBufs = 5;  // staged tiles: tile t + 4 loads while tile t is used
+
+// vmcnt(n) and lgkmcnt(0): at most n of this wave's vector-memory loads still
+// outstanding, and every LDS access of this wave complete.
+template <int n>
+__device__ __forceinline__ void wait_loads_lds() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0x0070 | (n & 15) | ((n >> 4) << 14));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 template <typename T, int D, bool CAUSAL>
-__global__ void __launch_bounds__(256, 1) bwd_dkdv_kernel(BwdParams p) {
+__global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
   using H = Half<T>;
   using Frag = typename H::Frag;
   using Pair = typename H::Pair;
   using Ops = TileOps<T, D>;
-  constexpr int RB = 2 * D;
-  constexpr int TILE = kBwdTile * RB;
+  constexpr int RB = 2 * D, CPR = D / 8, RPL = 1024 / RB;
+  constexpr int QT = kDkvQ;
+  constexpr int NB = kDkvBufs;
+  constexpr int TILE = QT * RB;   // bytes of one staged Q (or dO) tile
+  constexpr int CH = TILE / 1024;  // 1 KiB pieces per tensor and tile
+  constexpr int LPW = 2 * CH / 8;  // pieces (Q's, then dO's) each wave loads
+  static_assert(LPW >= 1 && LPW * 8 == 2 * CH, "tile split");
   constexpr int NKS = D / 16;
   constexpr int ND = D / 32;
-  __shared__ __attribute__((aligned(1024))) char smem[2][2][TILE];  // [buffer][Q, dO]
-  __shared__ __attribute__((aligned(16))) float stat[2][2][kBwdTile];  // [buffer][LSE, D]
+  __shared__ __attribute__((aligned(1024))) char smem[NB][2][TILE];  // [buffer][Q, dO]
+  __shared__ __attribute__((aligned(16))) float stat[NB][2][QT];     // [buffer][LSE log2 e, D]
+  // P of the current tile, per key group and slot (tile parity): 4 chunks of
+  // 64 lanes x 4 floats, so each 16-byte access of a wave covers 1 KiB.
+  __shared__ __attribute__((aligned(1024))) float xch[4][2][4][64 * 4];
 
   const int64_t N = p.N;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool prole = wave < 4;
+  const int kg = wave & 3;
   const int l32 = lane & 31, hh = lane >> 5;
-  // XCD-aware order (the blocks of one head share an XCD's L2); causal:
-  // the blocks with the most queries (lowest keys) first.
+  // XCD-aware order (the blocks of one head share an XCD's L2).
   const int logical = xcd_order();
   const int64_t bh = logical / p.n_blk;
   const int kblk = logical % p.n_blk;
   const int64_t k0 = (int64_t)kblk * kBwdRows;
-  const int64_t kw = k0 + 32 * wave;  // this wave's first key
-  const int64_t key = kw + l32;       // this lane's key (B-operand column)
+  const int64_t kw = k0 + 32 * kg;  // the key group's first key
+  const int64_t key = kw + l32;     // this lane's key (B-operand column)
 
   const T* Qh = (const T*)p.q + bh * N * D;
-  const T* Kh = (const T*)p.k + bh * N * D;
-  const T* Vh = (const T*)p.v + bh * N * D;
   const T* dOh = (const T*)p.dout + bh * N * D;
-  const float* Lh = p.lse + bh * N;
+  const float* L2h = p.lse2 + bh * N;
   const float* Dh = p.delta + bh * N;
 
-  // K and V of this lane's key (B operands of S = Q K^T and dP = dO V^T).
-  Frag kf[NKS], vf[NKS];
+  // K (P wave) or V (dS wave) of this lane's key: B operand of S = Q K^T or
+  // dP = dO V^T.
+  Frag kv[NKS];
   {
     const bool ok = key < N;
-    const T* ks_ = Kh + (ok ? key : 0) * D + 8 * hh;
-    const T* vs_ = Vh + (ok ? key : 0) * D + 8 * hh;
+    const T* src = (prole ? (const T*)p.k : (const T*)p.v) + bh * N * D + (ok ? key : 0) * D + 8 * hh;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      kf[ks] = bits<Frag>(ok ? *(const u32x4*)(ks_ + 16 * ks) : u32x4{0, 0, 0, 0});
-      vf[ks] = bits<Frag>(ok ? *(const u32x4*)(vs_ + 16 * ks) : u32x4{0, 0, 0, 0});
-    }
+    for (int ks = 0; ks < NKS; ++ks)
+      kv[ks] = bits<Frag>(ok ? *(const u32x4*)(src + 16 * ks) : u32x4{0, 0, 0, 0});
   }
 
   // Query tiles: causal blocks start at the first tile holding a query >= k0.
-  const int qt_begin = CAUSAL ? (int)(k0 / kBwdTile) : 0;
-  const int qt_end = (int)((N + kBwdTile - 1) / kBwdTile);
-  const uint32_t lds_base = lds_addr(&smem[0][0][0]);
-  const uint32_t stat_base = lds_addr(&stat[0][0][0]);
+  const int qt_begin = CAUSAL ? (int)(k0 / QT) : 0;
+  const int qt_end = (int)((N + QT - 1) / QT);
+  const uint32_t lds_tiles = lds_addr(&smem[0][0][0]);
+  const uint32_t lds_stat = lds_addr(&stat[0][0][0]);
+  // Piece wave*LPW + j of a tile: lane i fills chunk slot i % CPR of row
+  // (piece % CH)*RPL + i / CPR, which holds that row's chunk slot ^ swizzle.
+  int goff[LPW];
+#pragma unroll
+  for (int j = 0; j < LPW; ++j) {
+    const int r = ((wave * LPW + j) % CH) * RPL + lane / CPR;
+    goff[j] = r * RB + bswz<D>(r, lane % CPR) * 16;
+  }
+  // Tiles past the end are still issued, over an empty range (every lane
+  // reads zero), so that each wave issues the same number of loads per tile
+  // and the wait counts below are constants.
   auto issue = [&](int qt) {
-    if (qt >= qt_end) return;
-    const int buf = qt & 1;
-    const int64_t r0 = (int64_t)qt * kBwdTile;
-    stage_tile<D, 4>(Qh + r0 * D, 0, N - r0, lds_base + (buf * 2 + 0) * TILE, wave, lane);
-    stage_tile<D, 4>(dOh + r0 * D, 0, N - r0, lds_base + (buf * 2 + 1) * TILE, wave, lane);
-    if (wave == 0 && lane < 16) {  // 64 floats each: 16 lanes x 16 bytes
-      const uint32_t rows = (uint32_t)(N - r0 < kBwdTile ? N - r0 : kBwdTile);
-      dma_load16(buffer_rsrc(Lh + r0, rows * 4), stat_base + (buf * 2 + 0) * kBwdTile * 4, lane * 16);
-      dma_load16(buffer_rsrc(Dh + r0, rows * 4), stat_base + (buf * 2 + 1) * kBwdTile * 4, lane * 16);
+    const int buf = qt % NB;
+    const int64_t r0 = (int64_t)qt * QT;
+    const bool real = qt < qt_end;
+    const uint32_t rows = real ? (uint32_t)(N - r0 < QT ? N - r0 : QT) : 0u;
+    const int64_t base = real ? r0 : 0;
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+      const int piece = wave * LPW + j;
+      const T* head = piece < CH ? Qh : dOh;
+      dma_load16(buffer_rsrc(head + base * D, rows * RB),
+                 lds_tiles + (buf * 2 + piece / CH) * TILE + (piece % CH) * 1024, goff[j]);
+    }
+    if (wave == 0 && lane < QT / 4) {  // 32 floats each: 8 lanes x 16 bytes
+      dma_load16(buffer_rsrc(L2h + base, rows * 4), lds_stat + (buf * 2 + 0) * QT * 4, lane * 16);
+      dma_load16(buffer_rsrc(Dh + base, rows * 4), lds_stat + (buf * 2 + 1) * QT * 4, lane * 16);
     }
   };
 
-  f32x16 dk[ND], dv[ND];
+  f32x16 acc[ND];  // dV^T (P wave) or dK^T / scale (dS wave)
 #pragma unroll
-  for (int db = 0; db < ND; ++db) dk[db] = dv[db] = f32x16{};
+  for (int db = 0; db < ND; ++db) acc[db] = f32x16{};
   const float c = p.c;
   const int krow = k_row_of_lane(l32);
 
-  // The register loads above must land now: the compiler does not count the
-  // tile loads, so a wait it placed inside the loop would drain the prefetch.
-  issue(qt_begin);
-  wait_loads<0>();
+  // Tiles qt_begin .. qt_begin + NB - 2 before the loop; tile t + NB - 1 after
+  // the barrier of tile t.  The register loads above land with the first
+  // tile (the compiler does not count the tile loads, so a wait it placed
+  // inside the loop would drain the prefetch).
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    fence(kf[ks]);
-    fence(vf[ks]);
-  }
-  constexpr int LPW = TILE / 1024 / 4;  // loads per wave per tensor per tile
+  for (int j = 0; j < NB - 1; ++j) issue(qt_begin + j);
+  if (wave == 0)
+    wait_loads_lds<(NB - 2) * (LPW + 2)>();
+  else
+    wait_loads_lds<(NB - 2) * LPW>();
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) fence(kv[ks]);
+  block_barrier();
+
+  // The two roles run separate copies of the loop (same barriers), so that
+  // neither carries the other's registers.
+  auto tiles = [&](auto role) {
+  constexpr bool PW = decltype(role)::value;
   for (int qt = qt_begin; qt < qt_end; ++qt) {
-    // Tile qt + 1 is loaded while tile qt is used; wave 0 also loads the
-    // tile's LSE and D.
-    if (qt + 1 < qt_end) {
-      issue(qt + 1);
-      if (wave == 0)
-        wait_loads<2 * LPW + 2>();
-      else
-        wait_loads<2 * LPW>();
-    } else {
-      wait_loads<0>();
-    }
-    block_barrier();
-    const int buf = qt & 1;
+    const int buf = qt % NB;
     const char* qtile = &smem[buf][0][0];
     const char* dotile = &smem[buf][1][0];
-    const float* lse_t = &stat[buf][0][0];
-    const float* d_t = &stat[buf][1][0];
-    const int64_t q0 = (int64_t)qt * kBwdTile;
+    float* xs = &xch[kg][qt & 1][0][0];
+    const int64_t qbase = (int64_t)qt * QT;
+    // live: some query of the tile sees a key of the group.  full: every
+    // (query, key) pair of the 32x32 block is visible.
+    const bool live = !CAUSAL || qbase + QT - 1 >= kw;
+    const bool full = qbase + QT <= N && kw + 32 <= N && (!CAUSAL || qbase >= kw + 31);
+    // Register r of a lane holds query qbase + key_of_reg(r, hh) of its key;
+    // rows r = 8*half + e are the 8 consecutive queries 16*half + 8*hh + e.
+    Frag pf[2];
+    f32x16 dp;
+    Frag at[2 * ND];  // A operands of the dV (dO^T) or dK (Q^T) products
+    if (live) {
+      if constexpr (PW) {
+        // All A operands of S are read before the products, and the dO^T
+        // operands of the dV products (same tile) right after them, so LDS
+        // latency is paid once per group instead of once per product.
+        Frag a[NKS];
 #pragma unroll
-    for (int qb = 0; qb < kBwdTile / 32; ++qb) {
-      const int64_t qbase = q0 + 32 * qb;
-      if (CAUSAL && qbase + 31 < kw) continue;  // every query of the block precedes the wave's keys
-      if (qbase >= N) continue;
-      // S = Q K^T, dP = dO V^T: register r of the lane holds query
-      // qbase + key_of_reg(r, hh) and key `key` (A rows fed permuted).
-      f32x16 s = f32x16{}, dp = f32x16{};
+        for (int ks = 0; ks < NKS; ++ks) a[ks] = Ops::row(qtile, krow, 2 * ks + hh);
+        __builtin_amdgcn_sched_group_barrier(0x100, NKS, 0);
+        f32x16 s = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        s = H::mma(Ops::row(qtile, 32 * qb + krow, 2 * ks + hh), kf[ks], s);
-        dp = H::mma(Ops::row(dotile, 32 * qb + krow, 2 * ks + hh), vf[ks], dp);
-      }
-      float lse2[16], dl[16];
+        for (int ks = 0; ks < NKS; ++ks) s = H::mma(a[ks], kv[ks], s);
+        __builtin_amdgcn_sched_group_barrier(0x008, NKS, 0);
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int qi = 32 * qb + 16 * half + 8 * hh;  // 8 consecutive queries
-        const float4 a0 = *(const float4*)(lse_t + qi), a1 = *(const float4*)(lse_t + qi + 4);
-        const float4 b0 = *(const float4*)(d_t + qi), b1 = *(const float4*)(d_t + qi + 4);
-        const float la[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-        const float lb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+        for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          lse2[8 * half + e] = la[e] * kLog2e;
-          dl[8 * half + e] = lb[e];
+          for (int db = 0; db < ND; ++db) at[jj * ND + db] = Ops::rows_t(dotile, 16 * jj, db, lane);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 * ND, 0);
+        const float* l2t = &stat[buf][0][0];
+        float pr[16];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int qi = 16 * half + 8 * hh;
+          const float4 a0 = *(const float4*)(l2t + qi), a1 = *(const float4*)(l2t + qi + 4);
+          const float la[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            pr[8 * half + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * half + e], c, -la[e]));
         }
-      }
-      Frag pf[2], sf[2];
+        if (!full) {
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        u32x4 fp, fs;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float pv[2], sv[2];
-#pragma unroll
-          for (int x = 0; x < 2; ++x) {
-            const int r = 8 * jj + 2 * e + x;
-            const int64_t qi = qbase + key_of_reg(r, hh);
-            const bool vis = qi < N && key < N && (!CAUSAL || key <= qi);
-            const float pr = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2[r])) : 0.f;
-            pv[x] = pr;
-            sv[x] = pr * (dp[r] - dl[r]);
+          for (int r = 0; r < 16; ++r) {
+            const int64_t q = qbase + key_of_reg(r, hh);
+            if (!(q < N && key < N && (!CAUSAL || key <= q))) pr[r] = 0.f;
           }
-          fp[e] = bits<uint32_t>(H::pack(pv[0], pv[1]));
-          fs[e] = bits<uint32_t>(H::pack(sv[0], sv[1]));
         }
-        pf[jj] = bits<Frag>(fp);
-        sf[jj] = bits<Frag>(fs);
+#pragma unroll
+        for (int ch = 0; ch < 4; ++ch)
+          *(float4*)(xs + ch * 256 + lane * 4) =
+              float4{pr[4 * ch], pr[4 * ch + 1], pr[4 * ch + 2], pr[4 * ch + 3]};
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          u32x4 f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            f[e] = bits<uint32_t>(H::pack(pr[8 * jj + 2 * e], pr[8 * jj + 2 * e + 1]));
+          pf[jj] = bits<Frag>(f);
+        }
+      } else {
+        // As above: the dP operands, then the Q^T operands of the dK products.
+        Frag a[NKS];
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) a[ks] = Ops::row(dotile, krow, 2 * ks + hh);
+        __builtin_amdgcn_sched_group_barrier(0x100, NKS, 0);
+        dp = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) dp = H::mma(a[ks], kv[ks], dp);
+        __builtin_amdgcn_sched_group_barrier(0x008, NKS, 0);
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int db = 0; db < ND; ++db) at[jj * ND + db] = Ops::rows_t(qtile, 16 * jj, db, lane);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 * ND, 0);
       }
-      // dV^T += dO^T P, dK^T += Q^T dS (A operands: transposed tile reads).
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-        for (int db = 0; db < ND; ++db) {
-          dv[db] = H::mma(Ops::rows_t(dotile, 32 * qb + 16 * jj, db, lane), pf[jj], dv[db]);
-          dk[db] = H::mma(Ops::rows_t(qtile, 32 * qb + 16 * jj, db, lane), sf[jj], dk[db]);
-        }
     }
-    block_barrier();  // the buffer is refilled two tiles later
+    // Tile qt + 1 must have landed and this tile's P be written before the
+    // barrier; NB - 3 later tiles may still be in flight.
+    if (wave == 0)
+      wait_loads_lds<(NB - 3) * (LPW + 2)>();
+    else
+      wait_loads_lds<(NB - 3) * LPW>();
+    block_barrier();
+    issue(qt + NB - 1);  // into the buffer of tile qt - 1, whose last reads preceded the barrier
+    if (live) {
+      if constexpr (PW) {
+        // dV^T += dO^T P (A operand: transposing reads of dO).
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int db = 0; db < ND; ++db)
+            acc[db] = H::mma(at[jj * ND + db], pf[jj], acc[db]);
+      } else {
+        // dS = P (dP - D); masked and out-of-range entries have P = 0.
+        const float* dt = &stat[buf][1][0];
+        float pr[16], dl[16];
+#pragma unroll
+        for (int ch = 0; ch < 4; ++ch) {
+          const float4 x = *(const float4*)(xs + ch * 256 + lane * 4);
+          pr[4 * ch] = x.x;
+          pr[4 * ch + 1] = x.y;
+          pr[4 * ch + 2] = x.z;
+          pr[4 * ch + 3] = x.w;
+        }
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int qi = 16 * half + 8 * hh;
+          const float4 b0 = *(const float4*)(dt + qi), b1 = *(const float4*)(dt + qi + 4);
+          const float lb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) dl[8 * half + e] = lb[e];
+        }
+        Frag sf[2];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          u32x4 f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 8 * jj + 2 * e;
+            f[e] = bits<uint32_t>(H::pack(pr[r] * (dp[r] - dl[r]), pr[r + 1] * (dp[r + 1] - dl[r + 1])));
+          }
+          sf[jj] = bits<Frag>(f);
+        }
+        // dK^T += Q^T dS (A operand: transposing reads of Q).
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int db = 0; db < ND; ++db)
+            acc[db] = H::mma(at[jj * ND + db], sf[jj], acc[db]);
+      }
+    }
   }
+  };
+  if (prole)
+    tiles(std::true_type{});
+  else
+    tiles(std::false_type{});
+  // Drain the empty loads issued for tiles past the end.
+  wait_loads_lds<0>();
 
-  // dK = scale * dK^T^T, dV: lane `key`, register r of block db is d row
-  // db*32 + 8*(r/4) + 4*hh + r%4.
+  // dV (P wave) or dK = scale * acc (dS wave): lane `key`, register r of
+  // block db is d row db*32 + 8*(r/4) + 4*hh + r%4.
   if (key < N) {
-    T* dkd = (T*)p.dk + (bh * N + key) * D + 4 * hh;
-    T* dvd = (T*)p.dv + (bh * N + key) * D + 4 * hh;
+    T* dst = (T*)(prole ? p.dv : p.dk) + (bh * N + key) * D + 4 * hh;
+    const float f = prole ? 1.0f : p.scale;
 #pragma unroll
     for (int db = 0; db < ND; ++db)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const Pair a = H::pack(dk[db][4 * g] * p.scale, dk[db][4 * g + 1] * p.scale);
-        const Pair b = H::pack(dk[db][4 * g + 2] * p.scale, dk[db][4 * g + 3] * p.scale);
-        *(u32x2*)(dkd + db * 32 + 8 * g) = u32x2{bits<uint32_t>(a), bits<uint32_t>(b)};
-        const Pair e = H::pack(dv[db][4 * g], dv[db][4 * g + 1]);
-        const Pair f = H::pack(dv[db][4 * g + 2], dv[db][4 * g + 3]);
-        *(u32x2*)(dvd + db * 32 + 8 * g) = u32x2{bits<uint32_t>(e), bits<uint32_t>(f)};
+        const Pair a = H::pack(acc[db][4 * g] * f, acc[db][4 * g + 1] * f);
+        const Pair b = H::pack(acc[db][4 * g + 2] * f, acc[db][4 * g + 3] * f);
+        *(u32x2*)(dst + db * 32 + 8 * g) = u32x2{bits<uint32_t>(a), bits<uint32_t>(b)};
       }
   }
 }
@@ -490,6 +610,7 @@ hipError_t launch(const BwdArgs& a, hipStream_t stream) {
   p.dk = a.dk;
   p.dv = a.dv;
   p.delta = (float*)a.workspace;
+  p.lse2 = p.delta + a.BH * a.N;
   p.N = a.N;
   p.n_blk = (int32_t)((a.N + kBwdRows - 1) / kBwdRows);
   p.n_blk_q = (int32_t)((a.N + 32 * kBwdWavesQ - 1) / (32 * kBwdWavesQ));
@@ -502,7 +623,7 @@ hipError_t launch(const BwdArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)(a.BH * p.n_blk);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3(grid), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3(grid), dim3(512), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3((unsigned)(a.BH * p.n_blk_q)),

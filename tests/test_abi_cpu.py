@@ -343,3 +343,10 @@ def test_persistent_no_device_reported_not_crashed(L):
         pytest.skip("a GPU is present")
     assert _pers(L)[0] == 8
     assert _pers(L, nwg=3, causal=1)[0] == 8
+
+
+def test_bwd_workspace_size(L):
+    """D and LSE * log2(e) per row: 8 bytes per (b, h, row)."""
+    assert L.flash_attn_bwd_workspace_size(2, 3, 100) == 2 * 3 * 100 * 8
+    assert L.flash_attn_bwd_workspace_size(0, 3, 100) == 0
+    assert L.flash_attn_bwd_workspace_size(1 << 30, 1 << 20, 1 << 20) == -1
