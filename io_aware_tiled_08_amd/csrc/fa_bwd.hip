@@ -168,7 +168,7 @@ __device__ __forceinline__ void block_barrier() {
 // vector work the other issues matrix products.  Q/dO tiles and their LSE and
 // D rows are loaded into LDS kDkvBufs - 1 tiles ahead.
 constexpr int kDkvQ = 32;    // queries per staged tile
-constexpr int kDkvBufs = 5;  // staged tiles: tile t + 4 loads while tile t is used
+constexpr int kDkvBufs = 6;  // staged tiles: tile t + 5 loads while tile t is used
 
 // vmcnt(n) and lgkmcnt(0): at most n of this wave's vector-memory loads still
 // outstanding, and every LDS access of this wave complete.
@@ -248,8 +248,7 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
   // Tiles past the end are still issued, over an empty range (every lane
   // reads zero), so that each wave issues the same number of loads per tile
   // and the wait counts below are constants.
-  auto issue = [&](int qt) {
-    const int buf = qt % NB;
+  auto issue = [&](int qt, int buf) {
     const int64_t r0 = (int64_t)qt * QT;
     const bool real = qt < qt_end;
     const uint32_t rows = real ? (uint32_t)(N - r0 < QT ? N - r0 : QT) : 0u;
@@ -272,13 +271,43 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
   for (int db = 0; db < ND; ++db) acc[db] = f32x16{};
   const float c = p.c;
   const int krow = k_row_of_lane(l32);
-
-  // Tiles qt_begin .. qt_begin + NB - 2 before the loop; tile t + NB - 1 after
-  // the barrier of tile t.  The register loads above land with the first
-  // tile (the compiler does not count the tile loads, so a wait it placed
-  // inside the loop would drain the prefetch).
+  // Lane byte offsets inside a staged tile: row reads (A operands of S and
+  // dP) and transposing reads (A operands of dV and dK).  The tile loop is
+  // unrolled over the NB buffers, so each buffer's base folds into the
+  // instructions' immediate offsets.
+  int roff[NKS], toff[2 * ND][2];
 #pragma unroll
-  for (int j = 0; j < NB - 1; ++j) issue(qt_begin + j);
+  for (int ks = 0; ks < NKS; ++ks) roff[ks] = krow * RB + bswz<D>(krow, 2 * ks + hh) * 16;
+  {
+    const int g = lane >> 4, j = lane & 15;
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int db = 0; db < ND; ++db) {
+        const int col = db * 32 + 16 * (g & 1) + 4 * (j & 3);
+        const int cc = col >> 3, off = (col & 7) * 2;
+        const int ra = 16 * jj + 8 * hh + (j >> 2), rb = ra + 4;
+        toff[jj * ND + db][0] = ra * RB + bswz<D>(ra, cc) * 16 + off;
+        toff[jj * ND + db][1] = rb * RB + bswz<D>(rb, cc) * 16 + off;
+      }
+  }
+  auto row_frag = [&](const char* tile, int ks) -> Frag {
+    return bits<Frag>(*(const u32x4*)(tile + roff[ks]));
+  };
+  auto tr_frag = [&](const char* tile, int i) -> Frag {
+    const u32x2 lo = lds_read_tr(tile, toff[i][0]);
+    const u32x2 hi = lds_read_tr(tile, toff[i][1]);
+    return bits<Frag>(u32x4{lo[0], lo[1], hi[0], hi[1]});
+  };
+  float* xlane = &xch[kg][0][0][0] + lane * 4;  // this lane's P slots: + slot*1024 + chunk*256
+
+  // Tiles qt_begin .. qt_begin + NB - 2 before the loop (tile qt_begin + i
+  // in buffer i % NB); tile t + NB - 1 after the barrier of tile t.  The
+  // register loads above land with the first tile (the compiler does not
+  // count the tile loads, so a wait it placed inside the loop would drain the
+  // prefetch).
+#pragma unroll
+  for (int j = 0; j < NB - 1; ++j) issue(qt_begin + j, j);
   if (wave == 0)
     wait_loads_lds<(NB - 2) * (LPW + 2)>();
   else
@@ -287,43 +316,41 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
   for (int ks = 0; ks < NKS; ++ks) fence(kv[ks]);
   block_barrier();
 
-  // The two roles run separate copies of the loop (same barriers), so that
-  // neither carries the other's registers.
-  auto tiles = [&](auto role) {
-  constexpr bool PW = decltype(role)::value;
-  for (int qt = qt_begin; qt < qt_end; ++qt) {
-    const int buf = qt % NB;
+  // One tile.  Register r of a lane holds query qbase + key_of_reg(r, hh) of
+  // its key; rows r = 8*half + e are the 8 consecutive queries
+  // 16*half + 8*hh + e.
+  auto step = [&](auto role, auto bufc, int qt) {
+    constexpr bool PW = decltype(role)::value;
+    constexpr int buf = decltype(bufc)::value;
     const char* qtile = &smem[buf][0][0];
     const char* dotile = &smem[buf][1][0];
-    float* xs = &xch[kg][qt & 1][0][0];
+    float* xs = xlane + (buf & 1) * 1024;
     const int64_t qbase = (int64_t)qt * QT;
-    // live: some query of the tile sees a key of the group.  full: every
-    // (query, key) pair of the 32x32 block is visible.
-    const bool live = !CAUSAL || qbase + QT - 1 >= kw;
+    // live: some query of the tile sees a key of the group (always, when
+    // not causal; written as a run-time test there too, which keeps the
+    // compiler from merging the tiles of the unrolled loop into one region
+    // and spilling).  full: every (query, key) pair of the block is visible.
+    const bool live = CAUSAL ? qbase + QT - 1 >= kw : qbase < N;
     const bool full = qbase + QT <= N && kw + 32 <= N && (!CAUSAL || qbase >= kw + 31);
-    // Register r of a lane holds query qbase + key_of_reg(r, hh) of its key;
-    // rows r = 8*half + e are the 8 consecutive queries 16*half + 8*hh + e.
     Frag pf[2];
     f32x16 dp;
     Frag at[2 * ND];  // A operands of the dV (dO^T) or dK (Q^T) products
     if (live) {
+      // All A operands of S (or dP) are read before the products, and the
+      // transposed operands of the dV (or dK) products, same tile, right
+      // after them: LDS latency is paid once per group, not once per product.
+      Frag a[NKS];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) a[ks] = row_frag(PW ? qtile : dotile, ks);
+      __builtin_amdgcn_sched_group_barrier(0x100, NKS, 0);
+      f32x16 sd = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) sd = H::mma(a[ks], kv[ks], sd);
+      __builtin_amdgcn_sched_group_barrier(0x008, NKS, 0);
+#pragma unroll
+      for (int i = 0; i < 2 * ND; ++i) at[i] = tr_frag(PW ? dotile : qtile, i);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4 * ND, 0);
       if constexpr (PW) {
-        // All A operands of S are read before the products, and the dO^T
-        // operands of the dV products (same tile) right after them, so LDS
-        // latency is paid once per group instead of once per product.
-        Frag a[NKS];
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) a[ks] = Ops::row(qtile, krow, 2 * ks + hh);
-        __builtin_amdgcn_sched_group_barrier(0x100, NKS, 0);
-        f32x16 s = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) s = H::mma(a[ks], kv[ks], s);
-        __builtin_amdgcn_sched_group_barrier(0x008, NKS, 0);
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-          for (int db = 0; db < ND; ++db) at[jj * ND + db] = Ops::rows_t(dotile, 16 * jj, db, lane);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4 * ND, 0);
         const float* l2t = &stat[buf][0][0];
         float pr[16];
 #pragma unroll
@@ -333,19 +360,26 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
           const float la[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            pr[8 * half + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[8 * half + e], c, -la[e]));
+            pr[8 * half + e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sd[8 * half + e], c, -la[e]));
         }
-        if (!full) {
+        if (__builtin_expect(!full, 0)) {
+          // Query qbase + kr (kr = key_of_reg(r, hh)) is visible iff
+          // kr < N - qbase, and, when causal, kr >= key - qbase.  The bounds
+          // are clamped to [0, QT] and shifted by 8*hh so that kr becomes the
+          // constant key_of_reg(r, 0).
+          const int64_t hi64 = key < N ? N - qbase : 0;
+          const int hi = (int)(hi64 > QT ? QT : hi64) - 8 * hh;
+          const int64_t lo64 = CAUSAL ? key - qbase : 0;
+          const int lo = (int)(lo64 < 0 ? 0 : (lo64 > QT ? QT : lo64)) - 8 * hh;
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int64_t q = qbase + key_of_reg(r, hh);
-            if (!(q < N && key < N && (!CAUSAL || key <= q))) pr[r] = 0.f;
+            const int kr = key_of_reg(r, 0);
+            if (kr >= hi || kr < lo) pr[r] = 0.f;
           }
         }
 #pragma unroll
         for (int ch = 0; ch < 4; ++ch)
-          *(float4*)(xs + ch * 256 + lane * 4) =
-              float4{pr[4 * ch], pr[4 * ch + 1], pr[4 * ch + 2], pr[4 * ch + 3]};
+          *(float4*)(xs + ch * 256) = float4{pr[4 * ch], pr[4 * ch + 1], pr[4 * ch + 2], pr[4 * ch + 3]};
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
           u32x4 f;
@@ -355,20 +389,7 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
           pf[jj] = bits<Frag>(f);
         }
       } else {
-        // As above: the dP operands, then the Q^T operands of the dK products.
-        Frag a[NKS];
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) a[ks] = Ops::row(dotile, krow, 2 * ks + hh);
-        __builtin_amdgcn_sched_group_barrier(0x100, NKS, 0);
-        dp = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) dp = H::mma(a[ks], kv[ks], dp);
-        __builtin_amdgcn_sched_group_barrier(0x008, NKS, 0);
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-          for (int db = 0; db < ND; ++db) at[jj * ND + db] = Ops::rows_t(qtile, 16 * jj, db, lane);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4 * ND, 0);
+        dp = sd;
       }
     }
     // Tile qt + 1 must have landed and this tile's P be written before the
@@ -378,22 +399,22 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
     else
       wait_loads_lds<(NB - 3) * LPW>();
     block_barrier();
-    issue(qt + NB - 1);  // into the buffer of tile qt - 1, whose last reads preceded the barrier
+    // Into the buffer of tile qt - 1, whose last reads preceded the barrier.
+    issue(qt + NB - 1, (buf + NB - 1) % NB);
     if (live) {
       if constexpr (PW) {
-        // dV^T += dO^T P (A operand: transposing reads of dO).
+        // dV^T += dO^T P.
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-          for (int db = 0; db < ND; ++db)
-            acc[db] = H::mma(at[jj * ND + db], pf[jj], acc[db]);
+          for (int db = 0; db < ND; ++db) acc[db] = H::mma(at[jj * ND + db], pf[jj], acc[db]);
       } else {
         // dS = P (dP - D); masked and out-of-range entries have P = 0.
         const float* dt = &stat[buf][1][0];
         float pr[16], dl[16];
 #pragma unroll
         for (int ch = 0; ch < 4; ++ch) {
-          const float4 x = *(const float4*)(xs + ch * 256 + lane * 4);
+          const float4 x = *(const float4*)(xs + ch * 256);
           pr[4 * ch] = x.x;
           pr[4 * ch + 1] = x.y;
           pr[4 * ch + 2] = x.z;
@@ -418,16 +439,33 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
           }
           sf[jj] = bits<Frag>(f);
         }
-        // dK^T += Q^T dS (A operand: transposing reads of Q).
+        // dK^T += Q^T dS.
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-          for (int db = 0; db < ND; ++db)
-            acc[db] = H::mma(at[jj * ND + db], sf[jj], acc[db]);
+          for (int db = 0; db < ND; ++db) acc[db] = H::mma(at[jj * ND + db], sf[jj], acc[db]);
       }
     }
-  }
   };
+  // The two roles run separate copies of the loop (same barriers), so that
+  // neither carries the other's registers; each copy is unrolled over the NB
+  // buffers (tile qt_begin + i uses buffer i % NB and P slot i % 2).
+  auto tiles = [&](auto role) {
+    for (int qt0 = qt_begin; qt0 < qt_end; qt0 += NB) {
+      step(role, std::integral_constant<int, 0>{}, qt0);
+      if (qt0 + 1 >= qt_end) break;
+      step(role, std::integral_constant<int, 1>{}, qt0 + 1);
+      if (qt0 + 2 >= qt_end) break;
+      step(role, std::integral_constant<int, 2>{}, qt0 + 2);
+      if (qt0 + 3 >= qt_end) break;
+      step(role, std::integral_constant<int, 3>{}, qt0 + 3);
+      if (qt0 + 4 >= qt_end) break;
+      step(role, std::integral_constant<int, 4>{}, qt0 + 4);
+      if (qt0 + 5 >= qt_end) break;
+      step(role, std::integral_constant<int, 5>{}, qt0 + 5);
+    }
+  };
+  static_assert(NB == 6, "the tile loop above is written out for six buffers");
   if (prole)
     tiles(std::true_type{});
   else
