@@ -502,7 +502,8 @@ __global__ void __launch_bounds__(kBwdWavesQ * 64, 1) bwd_dq_kernel(BwdParams p)
   constexpr int TILE = kBwdTile * RB;
   constexpr int NKS = D / 16;
   constexpr int ND = D / 32;
-  __shared__ __attribute__((aligned(1024))) char smem[2][2][TILE];  // [buffer][K, V]
+  constexpr int NBQ = 3;  // K/V tiles in LDS: tile t + 2 loads while tile t is used
+  __shared__ __attribute__((aligned(1024))) char smem[NBQ][2][TILE];  // [buffer][K, V]
 
   const int64_t N = p.N;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -545,12 +546,15 @@ __global__ void __launch_bounds__(kBwdWavesQ * 64, 1) bwd_dq_kernel(BwdParams p)
   const int64_t wave_end = CAUSAL ? (qw + 32 < N ? qw + 32 : N) : N;
   const int wave_tiles = qw < N ? (int)((wave_end + kBwdTile - 1) / kBwdTile) : 0;
   const uint32_t lds_base = lds_addr(&smem[0][0][0]);
+  // Tiles past the end are issued over an empty range (every lane reads
+  // zero), so that each wave has the same loads in flight at every wait.
   auto issue = [&](int t) {
-    if (t >= n_tiles) return;
-    const int buf = t & 1;
-    const int64_t r0 = (int64_t)t * kBwdTile;
-    stage_tile<D, NWQ>(Kh + r0 * D, 0, N - r0, lds_base + (buf * 2 + 0) * TILE, wave, lane);
-    stage_tile<D, NWQ>(Vh + r0 * D, 0, N - r0, lds_base + (buf * 2 + 1) * TILE, wave, lane);
+    const int buf = t % NBQ;
+    const bool real = t < n_tiles;
+    const int64_t r0 = real ? (int64_t)t * kBwdTile : 0;
+    const int64_t rows = real ? N - r0 : 0;
+    stage_tile<D, NWQ>(Kh + r0 * D, 0, rows, lds_base + (buf * 2 + 0) * TILE, wave, lane);
+    stage_tile<D, NWQ>(Vh + r0 * D, 0, rows, lds_base + (buf * 2 + 1) * TILE, wave, lane);
   };
 
   f32x16 dq[ND];
@@ -559,8 +563,13 @@ __global__ void __launch_bounds__(kBwdWavesQ * 64, 1) bwd_dq_kernel(BwdParams p)
   const float c = p.c;
   const int krow = k_row_of_lane(l32);
 
+  // Tiles 0 and 1 before the loop, tile t + 2 after the barrier of tile t
+  // (into the buffer of tile t - 1, whose reads all precede that barrier).
+  // The register loads above land with tile 0.
+  constexpr int LPW = TILE / 1024 / NWQ;
   issue(0);
-  wait_loads<0>();
+  issue(1);
+  wait_loads<2 * LPW>();
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
     fence(qf[ks]);
@@ -568,17 +577,12 @@ __global__ void __launch_bounds__(kBwdWavesQ * 64, 1) bwd_dq_kernel(BwdParams p)
   }
   fence(lse2);
   fence(drow);
-  constexpr int LPW = TILE / 1024 / NWQ;
   for (int t = 0; t < n_tiles; ++t) {
-    if (t + 1 < n_tiles) {
-      issue(t + 1);
-      wait_loads<2 * LPW>();
-    } else {
-      wait_loads<0>();
-    }
+    wait_loads<2 * LPW>();  // tile t has landed; tile t + 1 may be in flight
     block_barrier();
+    issue(t + 2);
     if (t < wave_tiles) {
-      const int buf = t & 1;
+      const int buf = t % NBQ;
       const char* ktile = &smem[buf][0][0];
       const char* vtile = &smem[buf][1][0];
       const int64_t k0 = (int64_t)t * kBwdTile;
@@ -592,22 +596,30 @@ __global__ void __launch_bounds__(kBwdWavesQ * 64, 1) bwd_dq_kernel(BwdParams p)
           s = H::mma(Ops::row(ktile, 32 * kb + krow, 2 * ks + hh), qf[ks], s);
           dp = H::mma(Ops::row(vtile, 32 * kb + krow, 2 * ks + hh), df[ks], dp);
         }
+        float pr[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
+        // Key kbase + kr (kr = key_of_reg(r, hh)) is visible iff kr < N - kbase,
+        // the query exists, and, when causal, kr <= qrow - kbase.  The bound
+        // is shifted by 8*hh so that kr becomes the constant key_of_reg(r, 0).
+        const int64_t kbase = k0 + 32 * kb;
+        const bool full = kbase + 32 <= N && qw + 32 <= N && (!CAUSAL || kbase + 31 <= qw);
+        if (__builtin_expect(!full, 0)) {
+          int64_t hi64 = qrow < N ? N - kbase : 0;
+          if (CAUSAL && qrow - kbase + 1 < hi64) hi64 = qrow - kbase + 1;
+          const int hi = (int)(hi64 < 0 ? 0 : (hi64 > 32 ? 32 : hi64)) - 8 * hh;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (key_of_reg(r, 0) >= hi) pr[r] = 0.f;
+        }
         Frag sf[2];
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
           u32x4 fs;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            float sv[2];
-#pragma unroll
-            for (int x = 0; x < 2; ++x) {
-              const int r = 8 * jj + 2 * e + x;
-              const int64_t kj = k0 + 32 * kb + key_of_reg(r, hh);
-              const bool vis = kj < N && qrow < N && (!CAUSAL || kj <= qrow);
-              const float pr = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2)) : 0.f;
-              sv[x] = pr * (dp[r] - drow);
-            }
-            fs[e] = bits<uint32_t>(H::pack(sv[0], sv[1]));
+            const int r = 8 * jj + 2 * e;
+            fs[e] = bits<uint32_t>(H::pack(pr[r] * (dp[r] - drow), pr[r + 1] * (dp[r + 1] - drow)));
           }
           sf[jj] = bits<Frag>(fs);
         }
@@ -619,8 +631,8 @@ __global__ void __launch_bounds__(kBwdWavesQ * 64, 1) bwd_dq_kernel(BwdParams p)
             dq[db] = H::mma(Ops::rows_t(ktile, 32 * kb + 16 * jj, db, lane), sf[jj], dq[db]);
       }
     }
-    block_barrier();
   }
+  wait_loads<0>();  // the empty loads past the end land before the workgroup ends
 
   if (qrow < N) {
     T* dst = (T*)p.dq + (bh * N + qrow) * D + 4 * hh;
