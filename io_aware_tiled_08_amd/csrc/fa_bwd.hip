@@ -13,16 +13,20 @@
 // written to HBM.
 //
 // Three kernels, no atomics:
-//   * bwd_prep: D = rowsum(dO * O) per row, fp32, into the workspace.
-//   * bwd_dkdv: a workgroup owns 128 keys (4 waves x 32); it walks 64-query
-//     tiles of Q and dO (with their LSE and D) through LDS and accumulates
-//     dV^T += dO^T P and dK^T += Q^T dS in registers.  Scores are computed as
-//     S = Q K^T with K in registers, so a lane owns one key and the 16 queries
-//     of a 32x32 block sit in its registers; P and dS then feed the next
-//     products as B operands straight from those registers.
-//   * bwd_dq: a workgroup owns 128 queries; it walks 64-key tiles of K and V
-//     and accumulates dQ^T += K^T dS^T with S^T = K Q^T (lane = query, as in the
-//     forward kernel).
+//   * bwd_prep: D = rowsum(dO * O) and LSE * log2(e) per row, fp32, into the
+//     workspace.
+//   * bwd_dkdv: a workgroup owns 128 keys in four groups of 32 and runs eight
+//     waves; the two waves of a key group share a SIMD.  One ("P wave", K in
+//     registers) computes S = Q K^T, P and dV^T += dO^T P; the other ("dS
+//     wave", V in registers) computes dP = dO V^T, takes P from LDS and
+//     accumulates dK^T += Q^T dS.  With K (or V) as the B operand a lane owns
+//     one key and the 16 queries of a 32x32 block sit in its registers, so P
+//     and dS feed the next products as B operands straight from registers.
+//     32-query tiles of Q and dO (with their LSE and D) are staged through
+//     LDS five tiles ahead.
+//   * bwd_dq: a workgroup owns 256 queries (8 waves x 32); it walks 64-key
+//     tiles of K and V and accumulates dQ^T += K^T dS^T with S^T = K Q^T
+//     (lane = query, as in the forward kernel).
 // Every tile is read both by rows (MFMA A operands) and transposed
 // (ds_read_b64_tr_b16, for the d x rows operands); one XOR permutation of the
 // 16-byte chunks of a row serves both without LDS bank conflicts.
@@ -35,9 +39,9 @@
 namespace fa {
 namespace {
 
-constexpr int kBwdRows = 128;  // keys per dK/dV workgroup (4 waves x 32)
+constexpr int kBwdRows = 128;  // keys per dK/dV workgroup (4 key groups x 32)
 constexpr int kBwdWavesQ = 8;   // waves per dQ workgroup (32 queries each)
-constexpr int kBwdTile = 64;   // queries or keys per staged tile
+constexpr int kBwdTile = 64;   // keys per staged tile of the dQ kernel
 
 struct BwdParams {
   const void* q;
@@ -92,7 +96,7 @@ __global__ void __launch_bounds__(256) bwd_prep_kernel(BwdParams p, int64_t rows
   }
 }
 
-// Row-read and transposing-read helpers over a staged [kBwdTile x D] tile.
+// Row-read and transposing-read helpers over a staged [rows x D] tile.
 template <typename T, int D>
 struct TileOps {
   using Frag = typename Half<T>::Frag;
@@ -186,7 +190,6 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
   using H = Half<T>;
   using Frag = typename H::Frag;
   using Pair = typename H::Pair;
-  using Ops = TileOps<T, D>;
   constexpr int RB = 2 * D, CPR = D / 8, RPL = 1024 / RB;
   constexpr int QT = kDkvQ;
   constexpr int NB = kDkvBufs;

@@ -61,6 +61,17 @@ hand-derived two-key examples in tests/golden/), invariants (affine in V,
 permutations, shift of every key), pure-Python brute force for LSE on tiny
 inputs, and agreement of ``streaming_attention`` with ``attention_forward`` to
 1e-12.
+
+The later functions carry their derivations in their docstrings and are pinned
+in their own files: ``decode_e4m3``, ``dequantize_fp8`` and
+``fp8_weight_error_bound`` (tests/test_oracle_fp8.py: every e4m3 code against
+torch's float8_e4m3fn, fixed values, simulated weight rounding inside the
+bound); ``attention_backward`` and
+``backward_error_bound`` (tests/test_oracle_backward.py: torch autograd and
+SDPA in float64, central finite differences of ``attention_forward``,
+invariants, planted mistakes, simulated 16-bit rounding inside the bound);
+``attention_backward_sampled`` (the same file: equal to the full backward and
+bound at the chosen rows and columns).
 """
 from __future__ import annotations
 
@@ -413,3 +424,43 @@ def backward_error_bound(q, k, v, do, scale: float, causal: bool = False, u: flo
             bQ[b, h] = s64 * (e @ np.abs(K[b, h]))
             bK[b, h] = s64 * (e.T @ np.abs(Q[b, h]))
     return bQ, bK, bV
+
+
+def attention_backward_sampled(q, k, v, do, scale: float, causal: bool, heads, rows, cols,
+                               u: float = 2.0 ** -11, u_o: Optional[float] = None):
+    """attention_backward and backward_error_bound restricted to chosen
+    entries, for inputs too large to differentiate whole: for each (b, h) in
+    `heads`, dQ and its bound at query rows `rows`, and dK, dV and their
+    bounds at key rows `cols` (index arrays into N).
+
+    The definitions are those of attention_backward / backward_error_bound;
+    only the rows and columns of P, dP and dS that the chosen entries use are
+    formed into products (P itself is needed in full per head for D, since D
+    depends on every output row).  Returns {(b, h): (dQ[rows], dK[cols],
+    dV[cols], bQ[rows], bK[cols], bV[cols])}.
+    """
+    u_o = u if u_o is None else u_o
+    Q, K, V, dO = as_f64(q), as_f64(k), as_f64(v), as_f64(do)
+    B, H, N, d = Q.shape
+    s = boundary_scale(scale)
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    out = {}
+    for (b, h) in heads:
+        S = Q[b, h] @ K[b, h].T * s
+        if causal:
+            S[np.triu(np.ones((N, N), dtype=bool), 1)] = -np.inf
+        E = np.exp(S - S.max(axis=1, keepdims=True))
+        P = E / E.sum(axis=1, keepdims=True)
+        O = P @ V[b, h]
+        Dv = (dO[b, h] * O).sum(axis=1)
+        dD = u_o * np.abs(dO[b, h] * O).sum(axis=1)
+        # rows of dS (for dQ) and columns of dS (for dK); P's columns give dV
+        dS_r = P[rows] * (dO[b, h][rows] @ V[b, h].T - Dv[rows, None])
+        dS_c = P[:, cols] * (dO[b, h] @ V[b, h][cols].T - Dv[:, None])
+        e_r = P[rows] * dD[rows, None] + u * (np.abs(dS_r) + P[rows] * dD[rows, None])
+        e_c = P[:, cols] * dD[:, None] + u * (np.abs(dS_c) + P[:, cols] * dD[:, None])
+        out[(b, h)] = (s * (dS_r @ K[b, h]), s * (dS_c.T @ Q[b, h]), P[:, cols].T @ dO[b, h],
+                       abs(s) * (e_r @ np.abs(K[b, h])), abs(s) * (e_c.T @ np.abs(Q[b, h])),
+                       u * (P[:, cols].T @ np.abs(dO[b, h])))
+    return out

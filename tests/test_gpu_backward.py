@@ -94,3 +94,32 @@ def test_backward_workspace_and_dtype_errors():
     y = x.float()
     with pytest.raises(FlashAttnError, match="FA_ERR_DTYPE"):
         flash_attn_bwd(y, y, y, y, lse, y)
+
+
+def test_backward_headline_size_sampled():
+    """The benchmark's launch (B=2 H=16 N=4096 d=128 fp16, non-causal, O and
+    LSE from the fp64 forward): every output finite; four heads checked at 48
+    sampled query rows and 48 sampled key rows (plus the first and last)
+    against the sampled oracle and its bound."""
+    w = W.BWD_WORKLOADS["headline_bwd_f16_d128"]
+    q, k, v = W.random_qkv(w.B, w.H, w.N, w.d, w.dtype, w.seed)
+    do = W.random_dout(w.B, w.H, w.N, w.d, w.dtype, w.seed)
+    print(f"backward at B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype} causal={w.causal}", flush=True)
+    got = run_bwd(q, k, v, do, w.scale, w.causal, w.dtype)
+    for g in got:
+        assert torch.isfinite(g).all()
+    rng = np.random.default_rng([w.seed, 77])
+    rows = np.unique(np.concatenate([[0, w.N - 1], rng.choice(w.N, 48, replace=False)]))
+    cols = np.unique(np.concatenate([[0, w.N - 1], rng.choice(w.N, 48, replace=False)]))
+    heads = [(0, 0), (0, 7), (1, 8), (1, 15)]
+    u = UNIT[w.dtype]
+    ref = oracle.attention_backward_sampled(q, k, v, do, w.scale, w.causal, heads, rows, cols, u=u)
+    for (b, h), (rq, rk, rv, bq, bk, bv) in ref.items():
+        for name, g, r, bound in (("dQ", got[0][b, h][rows], rq, bq), ("dK", got[1][b, h][cols], rk, bk),
+                                  ("dV", got[2][b, h][cols], rv, bv)):
+            G = g.double().cpu().numpy()
+            tol = 1.2 * bound + u * np.abs(r) + 1e-5 * max(1.0, float(np.abs(r).max())) + 1e-6
+            err = np.abs(G - r)
+            print(f"head ({b},{h}) {name}: max|d|={err.max():.3e} max err/tol={float((err / tol).max()):.3f}",
+                  flush=True)
+            assert np.all(err <= tol), f"head ({b},{h}) {name}: outside the 16-bit backward bound"

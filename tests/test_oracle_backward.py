@@ -150,3 +150,22 @@ def test_backward_bound_holds_for_simulated_rounding(dtype, u, causal):
         assert np.all(err <= b * (1 + 1e-9) + 1e-13), name
         worst = max(worst, float(np.max(err / (b + 1e-300))))
     assert worst > 0.05
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_sampled_backward_is_the_full_one_restricted(causal):
+    """The sampled oracle used at full size returns exactly the chosen rows
+    and columns of the (torch-pinned) full gradients and bounds."""
+    q, k, v, do = (_randn(1500 + t, 2, 3, 41, 16) for t in range(4))
+    full = oracle.attention_backward(q, k, v, do, 0.4, causal)
+    bounds = oracle.backward_error_bound(q, k, v, do, 0.4, causal, u=2.0 ** -8)
+    rows, cols = np.array([0, 5, 17, 40]), np.array([1, 2, 33, 40, 39])
+    got = oracle.attention_backward_sampled(q, k, v, do, 0.4, causal, [(0, 0), (1, 2), (0, 1)],
+                                            rows, cols, u=2.0 ** -8)
+    for (b, h), (dq, dk, dv, bq, bk, bv) in got.items():
+        np.testing.assert_allclose(dq, full[0][b, h][rows], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(dk, full[1][b, h][cols], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(dv, full[2][b, h][cols], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(bq, bounds[0][b, h][rows], rtol=1e-12, atol=1e-15)
+        np.testing.assert_allclose(bk, bounds[1][b, h][cols], rtol=1e-12, atol=1e-15)
+        np.testing.assert_allclose(bv, bounds[2][b, h][cols], rtol=1e-12, atol=1e-15)
