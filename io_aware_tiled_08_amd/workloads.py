@@ -384,4 +384,7 @@ BWD_WORKLOADS = {
     "headline_bwd_f16_d128": BwdWorkload(
         "headline_bwd_f16_d128", 3, 2, 16, 4096, 128, "f16", False,
         description="backward of B=2 H=16 N=4096 d=128 fp16, N(0,1) inputs and dO, non-causal"),
+    "causal_bwd_bf16_d128": BwdWorkload(
+        "causal_bwd_bf16_d128", 6, 1, 16, 8192, 128, "bf16", True,
+        description="backward of B=1 H=16 N=8192 d=128 bf16, N(0,1) inputs and dO, causal"),
 }

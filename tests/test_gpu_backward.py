@@ -96,12 +96,14 @@ def test_backward_workspace_and_dtype_errors():
         flash_attn_bwd(y, y, y, y, lse, y)
 
 
-def test_backward_headline_size_sampled():
-    """The benchmark's launch (B=2 H=16 N=4096 d=128 fp16, non-causal, O and
-    LSE from the fp64 forward): every output finite; four heads checked at 48
-    sampled query rows and 48 sampled key rows (plus the first and last)
-    against the sampled oracle and its bound."""
-    w = W.BWD_WORKLOADS["headline_bwd_f16_d128"]
+@pytest.mark.parametrize("name", sorted(W.BWD_WORKLOADS))
+def test_backward_workload_sampled(name):
+    """The benchmark's launches at full size (B=2 H=16 N=4096 d=128 fp16
+    non-causal; B=1 H=16 N=8192 d=128 bf16 causal), O and LSE from the fp64
+    forward: every output finite; four heads checked at 48 sampled query rows
+    and 48 sampled key rows (plus the first and last) against the sampled
+    oracle and its bound."""
+    w = W.BWD_WORKLOADS[name]
     q, k, v = W.random_qkv(w.B, w.H, w.N, w.d, w.dtype, w.seed)
     do = W.random_dout(w.B, w.H, w.N, w.d, w.dtype, w.seed)
     print(f"backward at B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype} causal={w.causal}", flush=True)
@@ -111,7 +113,7 @@ def test_backward_headline_size_sampled():
     rng = np.random.default_rng([w.seed, 77])
     rows = np.unique(np.concatenate([[0, w.N - 1], rng.choice(w.N, 48, replace=False)]))
     cols = np.unique(np.concatenate([[0, w.N - 1], rng.choice(w.N, 48, replace=False)]))
-    heads = [(0, 0), (0, 7), (1, 8), (1, 15)]
+    heads = [(b, h) for b in range(w.B) for h in (0, w.H - 1)] + [(w.B - 1, w.H // 2)]
     u = UNIT[w.dtype]
     ref = oracle.attention_backward_sampled(q, k, v, do, w.scale, w.causal, heads, rows, cols, u=u)
     for (b, h), (rq, rk, rv, bq, bk, bv) in ref.items():
