@@ -195,7 +195,7 @@ __device__ __forceinline__ void fwd_f16_block(const KernelParams& p, const WorkI
   // (t = wave_tiles) no score product (m_s, m_pv).
   constexpr int NPV = NKB * 2 * ND;  // O^T += V^T P^T products
   constexpr int NS = NKS * NKB;      // S^T = K Q^T products
-  constexpr int kPipe = 4;
+  constexpr int kPipe = 3;
   auto fetch = [&](const char* vl, const char* kl, int i) -> Frag {
     if (i < NPV) {
       const int kb = i / (2 * ND), jj = (i / ND) % 2, db = i % ND;
