@@ -192,9 +192,9 @@ def summarize_traffic(fetch_csv: str, write_csv: str, workload: str) -> str:
     comp = w.compulsory_bytes()
     os.makedirs(PROFILES, exist_ok=True)
     lines = [
-        f"# HBM traffic of the forward kernel, workload {workload}",
+        f"# HBM traffic of the attention kernels, workload {workload}",
         "",
-        f"Workload: {w.description}.  Compulsory bytes (Q, K, V read once; O and fp32 LSE",
+        f"Workload: {w.description}.  Compulsory bytes (every input read once, every output",
         f"written once): {comp} ({comp / 2**20:.2f} MiB).  Kernels counted per call: "
         f"`{all_pat}*` (dispatches of `{main_pat}` = calls).",
         "",

@@ -1,0 +1,89 @@
+"""bench.py's host logic on a machine without a GPU: the one-GPU guard,
+workload lookup, the comment-blind source digest that keeps stored counters
+honest, the calibration arithmetic of the HBM-traffic summary, and the shape
+of the CPU-baseline record."""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+from io_aware_tiled_08_amd import workloads as W  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, cwd=ROOT, timeout=300)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_every_workload_has_a_kernel_key():
+    names = (list(W.WORKLOADS) + list(W.CACHE_WORKLOADS) + list(W.FP8_WORKLOADS)
+             + list(W.BWD_WORKLOADS))
+    for name in names:
+        w, key = bench.workload_by_name(name)
+        assert w.name == name
+        assert key in bench.KERNEL_SOURCES and key in bench.KERNEL_NAME_PATTERN
+    assert bench.workload_by_name("headline_f16_d128")[1] == "f16"
+    assert bench.workload_by_name("decode_long_bf16")[1] == "kvcache"
+    assert bench.workload_by_name("headline_bwd_f16_d128")[1] == "bwd"
+    with pytest.raises(SystemExit):
+        bench.workload_by_name("no_such_workload")
+
+
+def test_digest_ignores_comments_but_not_code(tmp_path, monkeypatch):
+    src = tmp_path / "csrc"
+    shutil.copytree(bench._CSRC, src)
+    monkeypatch.setattr(bench, "_CSRC", str(src))
+    base = bench.kernel_source_digest("bwd")
+    p = src / "fa_bwd.hip"
+    text = p.read_text()
+    p.write_text("// a new comment line\n" + text.replace("namespace fa {", "namespace fa {  /* x */\n\n", 1))
+    assert bench.kernel_source_digest("bwd") == base
+    p.write_text(text.replace("constexpr int kDkvQ = 32;", "constexpr int kDkvQ = 64;"))
+    assert bench.kernel_source_digest("bwd") != base
+    assert bench.kernel_source_digest("f16") != base
+
+
+def _pmc_csv(path, counter, rows):
+    with open(path, "w") as f:
+        f.write("Kernel_Name,Counter_Name,Counter_Value\n")
+        for name, value in rows:
+            f.write(f"{name},{counter},{value}\n")
+
+
+def test_traffic_summary_calibrates_against_the_copy(tmp_path, monkeypatch):
+    """Five calls of three kernels each; the 512 MiB calibration copies read
+    as a little over half their size for FETCH_SIZE (as the counter reports
+    for a device copy) and as their size for WRITE_SIZE; a small copy and an
+    unrelated kernel are ignored."""
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    copy_kib = bench.COPY_BYTES / 1024
+    fetch = [("bwd_prep_kernel", 10.0), ("bwd_dkdv_kernel", 1000.0), ("bwd_dq_kernel", 500.0)] * 5
+    fetch += [("elementwise_copy", copy_kib / 2 + 16.0)] * 3 + [("elementwise_copy", 4.0), ("other", 9e9)]
+    write = [("bwd_prep_kernel", 1.0), ("bwd_dkdv_kernel", 100.0), ("bwd_dq_kernel", 50.0)] * 5
+    write += [("elementwise_copy", copy_kib)] * 3
+    _pmc_csv(tmp_path / "f.csv", "FETCH_SIZE", fetch)
+    _pmc_csv(tmp_path / "w.csv", "WRITE_SIZE", write)
+    path = bench.summarize_traffic(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"),
+                                   "headline_bwd_f16_d128")
+    expect = 1510.0 * 1024 * copy_kib / (copy_kib / 2 + 16.0) + 151.0 * 1024
+    text = open(path).read()
+    assert f"hbm_bytes_per_launch: {expect:.0f}" in text
+    assert bench.measured_traffic("headline_bwd_f16_d128", "bwd") == pytest.approx(expect)
+    # a stored summary whose source hash no longer matches is ignored
+    open(path, "w").write(text.replace(bench.kernel_source_digest("bwd"), "0" * 64))
+    assert bench.measured_traffic("headline_bwd_f16_d128", "bwd") is None
+
+
+def test_cpu_baseline_record():
+    w = W.WORKLOADS["single_head_f32"]
+    q, k, v = W.workload_inputs(w)
+    rec = bench.cpu_baseline(w, q, k, v, 0.2)
+    assert rec["kind"] == "oracle" and rec["unit"] == "TFLOP/s"
+    assert rec["value"] > 0 and rec["cores"] >= 1 and w.name in rec["sample"]
