@@ -1,7 +1,7 @@
-// Device helpers shared by the fp16/bf16 kernels (the square forward kernel
-// and the key/value-cache kernel): MFMA wrappers per input type, the LDS
+// Device helpers shared by the 16-bit and 8-bit kernels (forward, key-split,
+// key/value cache, backward): MFMA wrappers per input type, the LDS
 // chunk permutation, transposing LDS reads, direct-to-LDS buffer loads,
-// register fences and a max tree.
+// register fences and two forms of a maximum over many values.
 #pragma once
 
 #include "fa_device.h"
@@ -139,6 +139,26 @@ __device__ __forceinline__ float tree_max(Get get) {
     const float z = tree_max<c>([&](int i) { return get(a + b + i); });
     return fmaxf(fmaxf(x, y), z);
   }
+}
+
+// Maximum of n values get(0..n-1) as four chains of three-input maxima
+// (v_max3_f32): (n - 1) / 2 + 2 instructions, against about 0.65 n for a
+// balanced tree; the chains are independent, so their latencies overlap.
+template <int n, typename Get>
+__device__ __forceinline__ float chain_max4(Get get) {
+  static_assert(n % 4 == 0 && n >= 12, "four chains of at least three values");
+  constexpr int L = n / 4;
+  float m[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    float x = __builtin_fmaxf(__builtin_fmaxf(get(c * L), get(c * L + 1)), get(c * L + 2));
+    int i = 3;
+#pragma unroll
+    for (; i + 1 < L; i += 2) x = __builtin_fmaxf(__builtin_fmaxf(x, get(c * L + i)), get(c * L + i + 1));
+    if (i < L) x = __builtin_fmaxf(x, get(c * L + i));
+    m[c] = x;
+  }
+  return __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(m[0], m[1]), m[2]), m[3]);
 }
 
 }  // namespace

@@ -52,26 +52,6 @@
 namespace fa {
 namespace {
 
-// Maximum of n values get(0..n-1) as four chains of three-input maxima
-// (v_max3_f32): (n - 1) / 2 + 2 instructions, against about 0.65 n for a
-// balanced tree; the chains are independent, so their latencies overlap.
-template <int n, typename Get>
-__device__ __forceinline__ float chain_max4(Get get) {
-  static_assert(n % 4 == 0 && n >= 12, "four chains of at least three values");
-  constexpr int L = n / 4;
-  float m[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    float x = __builtin_fmaxf(__builtin_fmaxf(get(c * L), get(c * L + 1)), get(c * L + 2));
-    int i = 3;
-#pragma unroll
-    for (; i + 1 < L; i += 2) x = __builtin_fmaxf(__builtin_fmaxf(x, get(c * L + i)), get(c * L + i + 1));
-    if (i < L) x = __builtin_fmaxf(x, get(c * L + i));
-    m[c] = x;
-  }
-  return __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(m[0], m[1]), m[2]), m[3]);
-}
-
 // One 256-row query block (work item wi) of one (batch, head): the whole
 // pass from the Q load to the O and LSE stores.  Every wave of the workgroup
 // calls it with the same wi; on return all LDS reads of the item are done

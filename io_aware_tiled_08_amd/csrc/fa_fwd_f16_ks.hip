@@ -249,7 +249,7 @@ __global__ void __launch_bounds__(512, 1) fwd_f16_ks_kernel(KernelParams p) {
           if (kb * 32 + key_of_reg(r, 0) >= lim) s[kb][r] = kNegInf;
     }
     // Row maximum as a tree (short dependency chains), then across halves.
-    float mx = tree_max<NKB * 16>([&](int i) { return s[i / 16][i % 16]; });
+    float mx = chain_max4<NKB * 16>([&](int i) { return s[i / 16][i % 16]; });
     mx = halves_max(mx);
     const float mxc = mx * c;  // c > 0, so -inf stays -inf
 

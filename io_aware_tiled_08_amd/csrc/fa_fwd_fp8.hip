@@ -308,7 +308,7 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Params p) {
         for (int r = 0; r < 16; ++r)
           if (64 * (kb >> 1) + 16 * (kb & 1) + r >= lim) s[kb][r] = kNegInf;
     }
-    float mx = tree_max<NKB * 16>([&](int i) { return s[i / 16][i % 16]; });
+    float mx = chain_max4<NKB * 16>([&](int i) { return s[i / 16][i % 16]; });
     mx = halves_max(mx);
     const float mxc = mx * c;  // c > 0, so -inf stays -inf
     const bool grow = mxc > m + kRescaleSlack;
