@@ -114,6 +114,19 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(lds_char*)const_cast<void*>(p);
 }
 
+// Issue priority of the calling wave (s_setprio).  In the kernels whose two
+// wave groups alternate between a matrix-product phase and a softmax phase,
+// the wave in its product phase runs at priority 1 and its SIMD partner at 0:
+// when both have an instruction ready, the matrix product (which shares the
+// SIMD's vector issue) goes first, and the softmax work fills the cycles in
+// between.  The scheduling barriers keep the compiler from moving work across.
+template <int P>
+__device__ __forceinline__ void wave_priority() {
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(P);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Register fences.  The compiler may move plain arithmetic across
 // s_barrier (only memory effects are ordered by it); an empty volatile asm
 // that reads and rewrites a value pins the computation of that value before

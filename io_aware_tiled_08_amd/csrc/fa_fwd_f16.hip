@@ -341,11 +341,13 @@ __device__ __forceinline__ void fwd_f16_block(const KernelParams& p, const WorkI
   // tiles t < wave_tiles only (causal waves above the diagonal stop early)
   // but takes part in every slot's barrier.
   auto iteration = [&](int t, auto mwork, auto vwork) {
+    wave_priority<1>();
     mwork();
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) fence(s[kb]);
 #pragma unroll
     for (int db = 0; db < ND; ++db) fence(o[db]);
+    wave_priority<0>();
     if (group_b) wait_loads();
     barrier();
     if (group_b) {

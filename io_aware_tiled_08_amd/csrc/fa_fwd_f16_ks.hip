@@ -314,11 +314,13 @@ __global__ void __launch_bounds__(512, 1) fwd_f16_ks_kernel(KernelParams p) {
   // awaited at the end of B's next M phase (slot 2j+3), before their first
   // reader (slot 2j+4).
   auto iteration = [&](int j, auto mwork, auto vwork) {
+    wave_priority<1>();
     mwork();
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) fence(s[kb]);
 #pragma unroll
     for (int db = 0; db < ND; ++db) fence(o[db]);
+    wave_priority<0>();
     if (group_b) wait_loads();
     barrier();
     if (group_b) {

@@ -346,11 +346,13 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Params p) {
   // The same slot schedule as the 16-bit kernel: group A runs M(t) while group
   // B runs V(t-1) and loads K(t+2), V(t+1); then they swap.
   auto iteration = [&](int t, auto mwork, auto vwork) {
+    wave_priority<1>();
     mwork();
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) fence(s[kb]);
 #pragma unroll
     for (int db = 0; db <= ND; ++db) fence(o[db]);
+    wave_priority<0>();
     if (group_b) wait_loads();
     barrier();
     if (group_b) {

@@ -111,6 +111,29 @@ def test_constant_v_and_dominant_key():
     assert torch.allclose(lse.cpu(), torch.full((1, 1, N), 60.0), atol=1e-3)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("jump", [5.0, 12.0, 15.5, 17.0, 40.0, 118.0, 124.0, 180.0])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_score_jump_in_later_tile(dtype, jump, causal):
+    """One key (in the third 128-key tile) whose score exceeds every earlier
+    score of its row by `jump` log2 units: the 16-bit kernels take a tile's
+    reference maximum from the tile before, so this key's weight reaches
+    2^jump against the old reference.  The sizes straddle the rescale slack
+    (2^8), the top of fp16 (2^16) and the point where a bf16 weight's bit
+    pattern reads as an fp16 NaN (2^121)."""
+    N, d, p = 700, 64, 300
+    g = torch.Generator().manual_seed(int(jump * 10) + causal)
+    q = 0.1 * torch.randn(1, 2, N, d, generator=g)
+    k = 0.1 * torch.randn(1, 2, N, d, generator=g)
+    q[..., 0] = 1.0
+    k[:, :, p, 0] = jump / np.log2(np.e)  # scale 1: natural-log score of about jump * ln 2
+    dt = {"f16": torch.float16, "bf16": torch.bfloat16}[dtype]
+    q, k = q.to(dt), k.to(dt)
+    v = torch.randn(1, 2, N, d, generator=g).to(dt)
+    o, lse = gpu_forward(q, k, v, 1.0, causal)
+    check(o, lse, q, k, v, 1.0, causal, dtype, label=f"{dtype} jump={jump} causal={causal}")
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
 def test_deterministic(dtype):
     q, k, v = W.random_qkv(2, 2, 777, 128, dtype, seed=3)
