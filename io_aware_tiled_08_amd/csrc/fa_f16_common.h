@@ -15,6 +15,9 @@ namespace {
 constexpr float kRescaleSlack = 8.0f;
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 template <typename T>
 struct Half;
@@ -35,6 +38,13 @@ struct Half<_Float16> {
     const Pair one = {(_Float16)1.0f, (_Float16)1.0f};
     return __builtin_amdgcn_fdot2(p, one, acc, false);
   }
+  // acc[r] + the sum of the four values in x, for every r: a 4x4x4 product
+  // (16 blocks, one per four lanes) with an all-ones A operand, in which each
+  // output column is one lane's own four B values.
+  static __device__ __forceinline__ f32x4 sum4(u32x2 x, f32x4 acc) {
+    const f16x4 ones = {(_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f, (_Float16)1.0f};
+    return __builtin_amdgcn_mfma_f32_4x4x4f16(ones, bits<f16x4>(x), acc, 0, 0, 0);
+  }
 };
 
 template <>
@@ -51,6 +61,10 @@ struct Half<__bf16> {
   static __device__ __forceinline__ float sum2(Pair p, float acc) {
     const Pair one = {(__bf16)1.0f, (__bf16)1.0f};
     return __builtin_amdgcn_fdot2_f32_bf16(p, one, acc, false);
+  }
+  static __device__ __forceinline__ f32x4 sum4(u32x2 x, f32x4 acc) {
+    const i16x4 ones = {0x3f80, 0x3f80, 0x3f80, 0x3f80};  // bf16 1.0
+    return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(ones, bits<i16x4>(x), acc, 0, 0, 0);
   }
 };
 

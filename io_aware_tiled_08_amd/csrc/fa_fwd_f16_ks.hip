@@ -160,7 +160,10 @@ __global__ void __launch_bounds__(512, 1) fwd_f16_ks_kernel(KernelParams p) {
   f32x16 s[NKB];
   Frag pf[NKB][2];
   float m = kNegInf;  // reference maximum of the row, log2 units
-  float l = 0.f;      // this lane's share of the row sum (keys it holds)
+  // This lane's share of the row sum (the keys it holds), accumulated on the
+  // matrix pipe next to the P V products of the same weights; element 0 is
+  // used (the product writes the same value to all four).
+  f32x4 lacc = f32x4{};
   const float c = p.c;
 
   // M phase of tile t: O += P(t-1) V(t-1), then S(t) = K(t) Q^T: NPV + NS
@@ -187,6 +190,11 @@ __global__ void __launch_bounds__(512, 1) fwd_f16_ks_kernel(KernelParams p) {
     if (i < NPV) {
       const int kb = i / (2 * ND), jj = (i / ND) % 2, db = i % ND;
       o[db] = H::mma(a, pf[kb][jj], o[db]);
+      if (db == ND - 1) {
+        const u32x4 w = bits<u32x4>(pf[kb][jj]);
+        lacc = H::sum4(u32x2{w[0], w[1]}, lacc);
+        lacc = H::sum4(u32x2{w[2], w[3]}, lacc);
+      }
     } else {
       const int j = i - NPV, ks = j / NKB, kb = j % NKB;
       s[kb] = H::mma(a, qf[ks], s[kb]);
@@ -215,7 +223,11 @@ __global__ void __launch_bounds__(512, 1) fwd_f16_ks_kernel(KernelParams p) {
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < NPV && i % ND == ND - 1) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);  // with the two row-sum products
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
     }
   };
   auto m_pv = [&](int j) {
@@ -260,7 +272,7 @@ __global__ void __launch_bounds__(512, 1) fwd_f16_ks_kernel(KernelParams p) {
     if (__ballot(grow)) {
       const float alpha = grow ? __builtin_amdgcn_exp2f(m - mxc) : 1.0f;
       m = grow ? mxc : m;
-      l *= alpha;
+      lacc *= alpha;
 #pragma unroll
       for (int db = 0; db < ND; ++db) o[db] *= alpha;
     }
@@ -268,37 +280,28 @@ __global__ void __launch_bounds__(512, 1) fwd_f16_ks_kernel(KernelParams p) {
     // weights are exp2(-inf) = 0 either way.
     const float m_use = m == kNegInf ? 0.f : m;
 
-    // P = exp2(c*s - m), rounded to T; l accumulates the rounded weights so
-    // that O's normalisation matches the weights P V actually used.  Masked
-    // scores are -inf and c > 0, so their weight is exp2(-inf) = 0.
-    // One partial sum per fragment keeps the sum chains short.
-    float rs[NKB * 2];
+    // P = exp2(c*s - m), rounded to T (the row sum is formed from these
+    // rounded weights in the next matrix phase, so O's normalisation matches
+    // the weights P V actually uses).  Masked scores are -inf and c > 0, so
+    // their weight is exp2(-inf) = 0.
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) {
         u32x4 f;
-        float acc = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * jj + 2 * i], c, -m_use));
           const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * jj + 2 * i + 1], c, -m_use));
-          const Pair pr = H::pack(e0, e1);
-          acc = H::sum2(pr, acc);
-          f[i] = bits<uint32_t>(pr);
+          f[i] = bits<uint32_t>(H::pack(e0, e1));
         }
-        rs[kb * 2 + jj] = acc;
         pf[kb][jj] = bits<Frag>(f);
       }
-    float rsum = 0.f;
-#pragma unroll
-    for (int i = 0; i < NKB * 2; ++i) rsum += rs[i];
-    l += rsum;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj) fence(pf[kb][jj]);
-    fence(l);
+    fence(lacc);
     fence(m);
   };
 
@@ -320,6 +323,7 @@ __global__ void __launch_bounds__(512, 1) fwd_f16_ks_kernel(KernelParams p) {
     for (int kb = 0; kb < NKB; ++kb) fence(s[kb]);
 #pragma unroll
     for (int db = 0; db < ND; ++db) fence(o[db]);
+    fence(lacc);
     wave_priority<0>();
     if (group_b) wait_loads();
     barrier();
@@ -355,7 +359,7 @@ __global__ void __launch_bounds__(512, 1) fwd_f16_ks_kernel(KernelParams p) {
   constexpr int OS = D + 4;  // row stride (floats) of a partial O
   float* mo = (float*)&smem[0][0][0];
   float* mstat = mo + 4 * 32 * OS;  // [row group][row]: m, then l
-  const float lt_g = halves_sum(l);
+  const float lt_g = halves_sum(lacc[0]);
   if (group_b) {
     float* ow = mo + (gw * 32 + l32) * OS + 4 * hh;
 #pragma unroll
