@@ -26,7 +26,8 @@
 //     and V^T rows 32h + j are read from row-major V in LDS with transposing
 //     8-bit reads (ds_read_b64_tr_b8).
 //   * The row sum l is the sum of the rounded weights, computed by the matrix
-//     unit: one more P V product per chunk against an all-ones A operand.
+//     unit: per chunk, one 16x16x128 product of the P fragment against a
+//     patterned ones operand, which gives every lane its own query's sum.
 //   * The softmax weights are at most 2^8 (the lazy-rescale slack) and the
 //     largest e4m3 value is 448, so rounding P never overflows.
 // Accuracy: every step is exact or fp32 except the rounding of the weights to
@@ -72,6 +73,19 @@ __device__ __forceinline__ f32x16 mma8(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
+// Row sums of a P^T fragment in the 32x32x64 B layout (lane l: query l%32,
+// keys 32*(l/32) .. +31 of the chunk), by one 16x16x128 product (same formats
+// and scales).  Read as a 16x16x128 B operand, lane l = n + 16g is column n of
+// k group g and holds query n + 16*(g%2), keys 32*(g/2) ..; the A operand
+// row m (lanes m + 16g) is all ones in the k groups g with g%2 == (m/4)%2 and
+// zero elsewhere.  Output row m, column n then sums both key halves of query
+// n + 16*((m/4)%2), and the 16x16 output layout puts rows 4(l/16) .. +3 of
+// column l%16 in lane l: the sum of lane l's own query l%32, in all four
+// registers.
+__device__ __forceinline__ f32x4 rowsum8(i32x8 sel_ones, i32x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sel_ones, b, c, 0, 0, 0, 127, 0, 127);
+}
+
 // Four floats to four e4m3 bytes (round to nearest even), first in byte 0.
 __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
@@ -112,7 +126,7 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Params p) {
   constexpr int NKB = BC / 32;     // 32-key score blocks per tile
   constexpr int NKC = BC / 64;     // 64-key chunks per tile (P V depth)
   constexpr int NKS = D / 64;      // MFMAs per score block
-  constexpr int ND = D / 32;       // 32-row blocks of O^T (block ND: row sums)
+  constexpr int ND = D / 32;       // 32-row blocks of O^T (product slot ND: row sums)
   constexpr int RPL = 1024 / RB;   // rows one wave-wide 1 KiB load covers
   constexpr int LPW = TILE / 1024 / 4;  // 1 KiB loads per loading wave per tensor
   static_assert(LPW >= 1 && TILE % 4096 == 0, "tile shape");
@@ -222,13 +236,16 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Params p) {
     for (int db = 0; db < ND; ++db)
       voff[db] = vrow * RB + Sw::v(vrow, 2 * db + (g & 1)) * 16 + 8 * (i16 & 1);
   }
-  const i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                      0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
+  // e4m3 1.0 in every byte of the lanes whose k group parity matches their
+  // output row block parity (rowsum8).
+  const int one_w = ((lane >> 4) & 1) == ((lane >> 2) & 1) ? 0x38383838 : 0;
+  const i32x8 ones = {one_w, one_w, one_w, one_w, one_w, one_w, one_w, one_w};
 
   // ---- running state ----------------------------------------------------------
-  f32x16 o[ND + 1];  // O^T blocks; block ND holds the row sum l in every register
+  f32x16 o[ND];        // O^T blocks
+  f32x4 lsum = f32x4{};  // the row sum l (every register holds it)
 #pragma unroll
-  for (int db = 0; db <= ND; ++db) o[db] = f32x16{};
+  for (int db = 0; db < ND; ++db) o[db] = f32x16{};
   f32x16 s[NKB];
   i32x8 pf[NKC];
   float m = kNegInf;  // reference maximum of the row, log2 units
@@ -259,7 +276,10 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Params p) {
   auto apply = [&](int i, i32x8 a) {
     if (i < NPV) {
       const int ch = i / (ND + 1), db = i % (ND + 1);
-      o[db] = mma8(a, pf[ch], o[db]);
+      if (db == ND)
+        lsum = rowsum8(a, pf[ch], lsum);
+      else
+        o[db] = mma8(a, pf[ch], o[db]);
     } else {
       const int j = i - NPV, ks = j / NKB, kb = j % NKB;
       s[kb] = mma8(a, qf[ks], s[kb]);
@@ -316,7 +336,8 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Params p) {
       const float alpha = grow ? __builtin_amdgcn_exp2f(m - mxc) : 1.0f;
       m = grow ? mxc : m;
 #pragma unroll
-      for (int db = 0; db <= ND; ++db) o[db] *= alpha;
+      for (int db = 0; db < ND; ++db) o[db] *= alpha;
+      lsum *= alpha;
     }
     const float m_use = m == kNegInf ? 0.f : m;
     // P = exp2(c*s - m), rounded to e4m3; byte j of chunk ch's operand is
@@ -351,7 +372,8 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Params p) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) fence(s[kb]);
 #pragma unroll
-    for (int db = 0; db <= ND; ++db) fence(o[db]);
+    for (int db = 0; db < ND; ++db) fence(o[db]);
+    fence(lsum);
     wave_priority<0>();
     if (group_b) wait_loads();
     barrier();
@@ -376,7 +398,7 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Params p) {
   if (!group_b) barrier();
 
   // ---- epilogue: O = O_acc * v_descale / l (bf16), LSE = (m + log2 l) ln 2 --
-  const float lt = o[ND][0];
+  const float lt = lsum[0];
   if (qrow < N) {
     const float inv = p.o_scale / lt;
     if (hh == 0) Lh[qrow] = (m + __builtin_amdgcn_logf(lt)) * kLn2;
