@@ -113,10 +113,15 @@ fa_status flash_attn_fwd(const void* q, const void* k, const void* v,
  * causal blocks longest first, dealt to the workgroups in a snake order
  * (workgroup g takes block r*G + g in even rounds and r*G + G-1-g in odd
  * ones, G the grid size); unmasked blocks head-major, a contiguous range of
- * them per XCD and round.  Each block is computed exactly as flash_attn_fwd's
- * 256-row kernel computes it, so o and lse are bitwise equal to that
- * kernel's (flash_attn_fwd itself takes another schedule for causal d = 64
- * problems with few blocks, whose rounding can differ in the last bit).
+ * them per XCD and round, and a workgroup runs its unmasked blocks back to
+ * back as one stream of key tiles (the next block's Q is loaded and the
+ * finished block's O stored while tiles are in flight).  Each block is
+ * computed exactly as flash_attn_fwd's 256-row kernel computes it, so o and
+ * lse are bitwise equal to that kernel's (flash_attn_fwd itself takes another
+ * schedule for causal d = 64 problems with few blocks, whose rounding can
+ * differ in the last bit).  flash_attn_fwd uses this schedule, with one
+ * workgroup per compute unit, for unmasked fp16 / bf16 problems with at least
+ * two blocks per compute unit.
  *
  * Arguments as for flash_attn_fwd, plus
  *   num_workgroups  resident workgroups; 0 = one per compute unit of the

@@ -178,10 +178,16 @@ fa_status flash_attn_fwd(const void* q, const void* k, const void* v, void* o, f
   if (st != FA_OK || empty) return st;
   st = check_device();
   if (st != FA_OK) return st;
+  int dev = 0;
+  (void)hipGetDevice(&dev);  // succeeded inside check_device
+  const int cus = g_cu_count[dev];
   (void)hipGetLastError();  // do not report an earlier, unrelated error
-  const hipError_t e = dtype == FA_F32 ? fa::launch_forward_f32(a, (hipStream_t)stream)
-                       : keysplit      ? fa::launch_forward_f16_keysplit(a, (hipStream_t)stream)
-                                       : fa::launch_forward_f16(a, (hipStream_t)stream);
+  const hipError_t e =
+      dtype == FA_F32 ? fa::launch_forward_f32(a, (hipStream_t)stream)
+      : keysplit      ? fa::launch_forward_f16_keysplit(a, (hipStream_t)stream)
+      : fa::use_stream(a.dtype, a.causal, a.BH, N, cus)
+          ? fa::launch_forward_f16_persistent(a, cus, (hipStream_t)stream)
+          : fa::launch_forward_f16(a, (hipStream_t)stream);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return FA_OK;
 }

@@ -57,4 +57,13 @@ inline bool use_keysplit(Dtype dtype, int d, bool causal, int64_t BH, int64_t N)
          BH * ((N + kRowsPerWorkgroupF16 - 1) / kRowsPerWorkgroupF16) <= 2 * 256;
 }
 
+// Whether flash_attn_fwd runs an unmasked fp16/bf16 problem on the persistent
+// schedule (one workgroup per CU, each running its 256-row blocks as one tile
+// stream): from two blocks per CU on, where the grid schedule pays every
+// block's pipeline fill and drain, Q load and O store in series.
+inline bool use_stream(Dtype dtype, bool causal, int64_t BH, int64_t N, int cus) {
+  return dtype != Dtype::F32 && !causal && cus > 0 &&
+         BH * ((N + kRowsPerWorkgroupF16 - 1) / kRowsPerWorkgroupF16) >= 2 * (int64_t)cus;
+}
+
 }  // namespace fa
