@@ -855,10 +855,14 @@ KernelParams make_params(const FwdArgs& a) {
 }
 
 // n_wg == 0: one workgroup per block; else the persistent kernel on n_wg
-// workgroups (1 <= n_wg <= blocks).
+// workgroups (1 <= n_wg <= blocks).  An unmasked persistent launch whose tile
+// stream would count more steps than an int holds takes the grid instead
+// (same results, bit for bit).
 template <typename T, int D, bool CAUSAL>
 hipError_t launch(const FwdArgs& a, int n_wg, hipStream_t stream) {
   const KernelParams p = make_params<T, D, CAUSAL>(a);
+  if (!CAUSAL && n_wg > 0 && (p.n_items + n_wg - 1) / n_wg * ((a.N + 127) / 128) > 0x7fffffff)
+    n_wg = 0;
   if (n_wg == 0)
     hipLaunchKernelGGL((fwd_f16_kernel<T, D, CAUSAL>), dim3((unsigned)p.n_items), dim3(512), 0,
                        stream, p);
