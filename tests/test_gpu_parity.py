@@ -116,11 +116,11 @@ def test_constant_v_and_dominant_key():
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_score_jump_in_later_tile(dtype, jump, causal):
     """One key (in the third 128-key tile) whose score exceeds every earlier
-    score of its row by `jump` log2 units: the 16-bit kernels take a tile's
-    reference maximum from the tile before, so this key's weight reaches
-    2^jump against the old reference.  The sizes straddle the rescale slack
-    (2^8), the top of fp16 (2^16) and the point where a bf16 weight's bit
-    pattern reads as an fp16 NaN (2^121)."""
+    score of its row by `jump` log2 units, so the running maximum rises by
+    that much in one tile and what was accumulated is rescaled by 2^-jump.
+    The sizes straddle the lazy-rescale slack (2^8, below which the reference
+    stays put and weights up to 2^jump enter P), the top of fp16 (2^16), and
+    factors that underflow fp32 (2^-124 is subnormal, 2^-180 is zero)."""
     N, d, p = 700, 64, 300
     g = torch.Generator().manual_seed(int(jump * 10) + causal)
     q = 0.1 * torch.randn(1, 2, N, d, generator=g)
@@ -225,3 +225,25 @@ def test_causal_d64_many_blocks(dtype):
     rows = np.sort(np.concatenate([W.sample_rows(2100, B, H, N, 40),
                                    np.broadcast_to(np.array([0, 255, 256, 1099]), (B, H, 4))], axis=2), axis=2)
     check(o, lse, q, k, v, scale, True, dtype, rows=rows, label=f"{dtype} causal d=64 640 blocks")
+
+
+@pytest.mark.parametrize("dtype,d,N,heads,scale", [
+    ("f16", 128, 1000, 128, None),   # 512 blocks of 256 rows: two per CU, ragged last block
+    ("bf16", 64, 1300, 128, None),   # 768 blocks: three per CU
+    ("f16", 64, 700, 256, -0.11),    # negative scale: Q's sign flip on every next-block load
+])
+def test_many_unmasked_blocks(dtype, d, N, heads, scale):
+    """Unmasked problems with at least two 256-row blocks per CU, where
+    flash_attn_fwd runs each workgroup's blocks as one tile stream: sampled
+    rows (plus every block's first and last rows) against the oracle."""
+    B, H = 2, heads // 2
+    q, k, v = W.random_qkv(B, H, N, d, dtype, seed=7000 + N)
+    scale = W.default_scale(d) if scale is None else scale
+    o, lse = gpu_forward(q, k, v, scale, False)
+    base = {0, N - 1} | {x for b in range(0, N, 256) for x in (b, b + 255) if x < N}
+    rng = np.random.default_rng([N, 17])
+    extra = rng.choice(N, size=min(N, 24), replace=False)
+    rows = np.array(sorted(base | {int(x) for x in extra}), dtype=np.int64)
+    rows = np.broadcast_to(rows, (B, H, rows.size))
+    check(o, lse, q, k, v, scale, False, dtype, rows=rows,
+          label=f"{dtype} d={d} N={N} B*H={heads} scale={scale:.3f}")
