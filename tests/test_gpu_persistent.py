@@ -98,14 +98,24 @@ def test_persistent_negative_and_zero_scale(scale):
 @pytest.mark.parametrize("name", ["headline_f16_d128", "long_context_bf16"])
 def test_persistent_workload_bitwise(name):
     """Full-size workloads: bitwise equal to the grid kernel, plus sampled
-    rows against the oracle."""
+    rows against the oracle.  flash_attn_fwd itself runs unmasked problems of
+    two or more blocks per CU on the persistent tile stream, so the grid
+    kernel's reference comes from the first batch entry alone, few enough
+    blocks for flash_attn_fwd to take the grid."""
     w = W.WORKLOADS[name]
     print(f"workload {name}: B={w.B} H={w.H} N={w.N} d={w.d} {w.dtype} causal={w.causal}",
           flush=True)
     q, k, v = (x.to(DEV) for x in W.workload_inputs(w))
     o, lse = run(flash_attn_fwd_persistent, q, k, v, w.scale, w.causal)
-    o2, lse2 = run(flash_attn_fwd, q, k, v, w.scale, w.causal)
-    assert torch.equal(o, o2) and torch.equal(lse, lse2), name
+    if w.causal:
+        o2, lse2 = run(flash_attn_fwd, q, k, v, w.scale, w.causal)
+        assert torch.equal(o, o2) and torch.equal(lse, lse2), name
+    else:
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        assert w.H * ((w.N + 255) // 256) < 2 * cus, "first batch entry must take the grid"
+        q1, k1, v1 = (x[:1].contiguous() for x in (q, k, v))
+        o2, lse2 = run(flash_attn_fwd, q1, k1, v1, w.scale, w.causal)
+        assert torch.equal(o[:1], o2) and torch.equal(lse[:1], lse2), name
     rows = W.sample_rows(w.seed, w.B, w.H, w.N, 64)
     check_oracle(o, lse, q.cpu(), k.cpu(), v.cpu(), w.scale, w.causal, w.dtype, name, rows=rows)
 
