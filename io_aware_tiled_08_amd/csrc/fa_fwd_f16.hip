@@ -52,13 +52,25 @@
 namespace fa {
 namespace {
 
-// One 256-row query block (work item wi) of one (batch, head): the whole
-// pass from the Q load to the O and LSE stores.  Every wave of the workgroup
-// calls it with the same wi; on return all LDS reads of the item are done
-// (the last statement before the stores is a workgroup barrier), so a
-// workgroup may call it again for its next item.
-template <typename T, int D, bool CAUSAL>
-__device__ __forceinline__ void fwd_f16_block(const KernelParams& p, const WorkItem wi) {
+// The whole pass from the Q load to the O and LSE stores, for one 256-row
+// query block (work item wi) of one (batch, head), or, with STREAM, for the
+// R unmasked items j0, j0 + stride, ... (head-major) run back to back as one
+// stream of key tiles.  Every wave of the workgroup calls it with the same
+// arguments; on return all LDS reads are done (the last statement before the
+// stores is a workgroup barrier), so a workgroup may call it again.
+//
+// The stream fills and drains the two-group pipeline once per workgroup
+// rather than once per item: the next item's Q is loaded during the last
+// softmax phase of the current one, and the finished item's O is stored
+// during the first softmax phase of the next.  Each item's arithmetic is the
+// single-item pass's (same products, same order), so O and LSE are bitwise
+// equal.  In the stream every wave computes every tile (rows past N are zeros
+// and never stored).
+template <typename T, int D, bool CAUSAL, bool STREAM>
+__device__ __forceinline__ void fwd_f16_tiles(const KernelParams& p, const WorkItem wi,
+                                              const int64_t j0, const int64_t stride,
+                                              const int R) {
+  static_assert(!(CAUSAL && STREAM), "the tile stream is for unmasked items");
   using H = Half<T>;
   using Frag = typename H::Frag;
   using Pair = typename H::Pair;
@@ -101,6 +113,54 @@ __device__ __forceinline__ void fwd_f16_block(const KernelParams& p, const WorkI
   const int64_t wave_end = CAUSAL ? (qw + 32 < N ? qw + 32 : N) : N;
   const int wave_tiles = qw < N ? (int)((wave_end + BC - 1) / BC) : 0;
 
+  // Stream positions.  Step g of the stream is tile g % n_tiles of item
+  // g / n_tiles.  Positions are tracked by cursors that advance one step at a
+  // time, so the loop divides nothing: the next item is the current one plus
+  // stride, split once into whole heads and query blocks.
+  const int total = R * n_tiles;  // steps of the stream
+  // Wave-uniform values, pinned to scalar registers.
+  auto uniform64 = [](int64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+  };
+  const int64_t s_bh = uniform64(stride / p.n_qblk);
+  const int s_qb = __builtin_amdgcn_readfirstlane((int)(stride % p.n_qblk));
+  auto next_item = [&](WorkItem w) {
+    w.bh += s_bh;
+    w.qblk += s_qb;
+    if (w.qblk >= p.n_qblk) {
+      w.qblk -= p.n_qblk;
+      w.bh += 1;
+    }
+    return w;
+  };
+  struct Cursor {
+    WorkItem w;  // item of the step
+    int t;       // tile of the step within the item
+    int g;       // step
+  };
+  WorkItem first;
+  first.bh = uniform64(j0 / p.n_qblk);
+  first.qblk = __builtin_amdgcn_readfirstlane((int)(j0 % p.n_qblk));
+  auto advance = [&](Cursor& cu) {
+    ++cu.g;
+    if (++cu.t == n_tiles) {
+      cu.t = 0;
+      cu.w = next_item(cu.w);
+    }
+  };
+  // Cursor of step cu.g + k (k >= 0), one item at a time.
+  auto ahead = [&](Cursor cu, int k) {
+    cu.g += k;
+    cu.t += k;
+    while (cu.t >= n_tiles) {
+      cu.t -= n_tiles;
+      cu.w = next_item(cu.w);
+    }
+    return cu;
+  };
+
   // ---- tile loads: global -> LDS, 16 bytes per lane -------------------------
   // Group B (four waves) loads every tile.  Load j of group-wave gw
   // covers rows (gw*LPW + j)*RPL .. +RPL of the tile; lane i fills LDS chunk
@@ -115,21 +175,41 @@ __device__ __forceinline__ void fwd_f16_block(const KernelParams& p, const WorkI
   }
   const uint32_t lds_k = lds_addr(&smem[0][0][0]) + gw * LPW * 1024;
   const uint32_t lds_v = lds_addr(&smem[1][0][0]) + gw * LPW * 1024;
-  auto issue_k = [&](int t) {
-    if (t >= n_tiles) return;
-    const int64_t k0 = (int64_t)t * BC;
+  // In the stream, K and V tiles are issued in stream order: the tile of step
+  // g goes to LDS buffer g % 2, and the V phase of step g issues K(g + 2) and
+  // V(g + 1), derived from the cursor sc of that V phase.
+  auto issue_step = [&](const void* base, uint32_t lds, const int* voffs, const Cursor cu) {
+    if (cu.g >= total) return;
+    const int64_t k0 = (int64_t)cu.t * BC;
     const uint32_t rows = (uint32_t)(N - k0 < BC ? N - k0 : BC);
-    const u32x4 rs = buffer_rsrc(Kh + k0 * D, rows * RB);
+    const u32x4 rs = buffer_rsrc((const T*)base + (cu.w.bh * N + k0) * D, rows * RB);
 #pragma unroll
-    for (int j = 0; j < LPW; ++j) dma_load16(rs, lds_k + (t & 1) * TILE + j * 1024, kvoff[j]);
+    for (int j = 0; j < LPW; ++j) dma_load16(rs, lds + (cu.g & 1) * TILE + j * 1024, voffs[j]);
+  };
+  Cursor sc{first, 0, 0};
+  auto issue_k = [&](int t) {
+    if constexpr (STREAM) {
+      issue_step(p.k, lds_k, kvoff, ahead(sc, t - sc.g));
+    } else {
+      if (t >= n_tiles) return;
+      const int64_t k0 = (int64_t)t * BC;
+      const uint32_t rows = (uint32_t)(N - k0 < BC ? N - k0 : BC);
+      const u32x4 rs = buffer_rsrc(Kh + k0 * D, rows * RB);
+#pragma unroll
+      for (int j = 0; j < LPW; ++j) dma_load16(rs, lds_k + (t & 1) * TILE + j * 1024, kvoff[j]);
+    }
   };
   auto issue_v = [&](int t) {
-    if (t >= n_tiles) return;
-    const int64_t k0 = (int64_t)t * BC;
-    const uint32_t rows = (uint32_t)(N - k0 < BC ? N - k0 : BC);
-    const u32x4 rs = buffer_rsrc(Vh + k0 * D, rows * RB);
+    if constexpr (STREAM) {
+      issue_step(p.v, lds_v, vvoff, ahead(sc, t - sc.g));
+    } else {
+      if (t >= n_tiles) return;
+      const int64_t k0 = (int64_t)t * BC;
+      const uint32_t rows = (uint32_t)(N - k0 < BC ? N - k0 : BC);
+      const u32x4 rs = buffer_rsrc(Vh + k0 * D, rows * RB);
 #pragma unroll
-    for (int j = 0; j < LPW; ++j) dma_load16(rs, lds_v + (t & 1) * TILE + j * 1024, vvoff[j]);
+      for (int j = 0; j < LPW; ++j) dma_load16(rs, lds_v + (t & 1) * TILE + j * 1024, vvoff[j]);
+    }
   };
   auto barrier = [] {
     __builtin_amdgcn_sched_barrier(0);
@@ -143,8 +223,28 @@ __device__ __forceinline__ void fwd_f16_block(const KernelParams& p, const WorkI
   };
 
   // Q (B operand of S^T = K Q^T): lane holds Q[qrow][16*ks + 8*hh .. +7].
+  // The stream loads each item's Q through a buffer resource that ends at row
+  // N (rows past it read as zeros), so that nothing waits for the data before
+  // the products that use it; only a negative scale (a sign flip of Q) reads
+  // it at once.
   Frag qf[NKS];
-  {
+  auto load_q = [&](const WorkItem w) {
+    const int64_t q0 = (int64_t)w.qblk * BR;
+    const int64_t rows = N - q0 < BR ? N - q0 : BR;
+    const auto rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((const T*)p.q + (w.bh * N + q0) * D), (short)0, (int)(rows * RB), 0x00020000);
+    const int off = (wave * 32 + l32) * RB + hh * 16;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+      qf[ks] = bits<Frag>(__builtin_amdgcn_raw_buffer_load_b128(rs, off, 32 * ks, 0));
+    if (p.q_sign) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) qf[ks] = bits<Frag>(bits<u32x4>(qf[ks]) ^ p.q_sign);
+    }
+  };
+  if constexpr (STREAM) {
+    load_q(first);
+  } else {
     const bool ok = qrow < N;
     const T* src = Qh + (ok ? qrow : 0) * D + hh * 8;
 #pragma unroll
@@ -190,12 +290,33 @@ __device__ __forceinline__ void fwd_f16_block(const KernelParams& p, const WorkI
   f32x4 lacc = f32x4{};
   const float c = p.c;
 
+  // Epilogue of the stream's item w: O = O_acc / l, written once; LSE =
+  // (m + log2 l) * ln 2.
+  auto store = [&](const WorkItem w) {
+    const int64_t qrow = (int64_t)w.qblk * BR + (int64_t)wave * 32 + l32;
+    const float lt = halves_sum(lacc[0]);
+    if (qrow < N) {
+      const float inv = 1.0f / lt;
+      if (hh == 0) p.lse[w.bh * N + qrow] = (m + __builtin_amdgcn_logf(lt)) * kLn2;
+      T* dst = (T*)p.o + (w.bh * N + qrow) * D + hh * 4;
+#pragma unroll
+      for (int db = 0; db < ND; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const Pair lo = H::pack(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
+          const Pair hi = H::pack(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+          *(u32x2*)(dst + db * 32 + g * 8) = u32x2{bits<uint32_t>(lo), bits<uint32_t>(hi)};
+        }
+    }
+  };
+
   // M phase of tile t: O += P(t-1) V(t-1), then S(t) = K(t) Q^T: NPV + NS
   // matrix products whose A operands come from LDS.  In the steady state
   // (m_pv_s) the operand reads run kPipe products ahead of the products, so
   // LDS latency hides under the matrix pipe; the sched_group_barrier pairs
   // pin that order.  A wave's first tile has no P V product and its last
-  // (t = wave_tiles) no score product (m_s, m_pv).
+  // (t = wave_tiles, or g = total in the stream) no score product (m_s,
+  // m_pv).
   constexpr int NPV = NKB * 2 * ND;  // O^T += V^T P^T products
   constexpr int NS = NKS * NKB;      // S^T = K Q^T products
   constexpr int kPipe = 3;
@@ -267,8 +388,25 @@ __device__ __forceinline__ void fwd_f16_block(const KernelParams& p, const WorkI
     for (int i = NPV; i < NPV + NS; ++i) apply(i, fetch(kl, kl, i));
   };
 
-  // V phase of tile t: online softmax of S(t) into P(t).
-  auto v_phase = [&](int t) {
+  // V phase of tile t: online softmax of S(t) into P(t).  In the stream the
+  // tile comes from the cursor sc; the first step of an item first stores the
+  // previous item (its last P V product ran in the M phase just before) and
+  // starts the running state afresh, and the last step of an item loads the
+  // next item's Q (the last product that reads Q ran in the M phase just
+  // before).
+  WorkItem done = first;  // the stream's item before sc's (valid once sc.g >= n_tiles)
+  auto v_phase = [&](int t_arg) {
+    int t = t_arg;
+    if constexpr (STREAM) {
+      t = sc.t;
+      if (t == 0 && sc.g > 0) {
+        store(done);
+#pragma unroll
+        for (int db = 0; db < ND; ++db) o[db] = f32x16{};
+        lacc = f32x4{};
+        m = kNegInf;
+      }
+    }
     const int64_t k0 = (int64_t)t * BC;
     // Keys k0 + i with i >= lim are invisible (past N, or after the query
     // when causal): their scores become -inf.  Register r of key block kb
@@ -327,6 +465,13 @@ __device__ __forceinline__ void fwd_f16_block(const KernelParams& p, const WorkI
       for (int jj = 0; jj < 2; ++jj) fence(pf[kb][jj]);
     fence(lacc);
     fence(m);
+    if constexpr (STREAM) {
+      if (t == n_tiles - 1) {
+        done = sc.w;
+        if (sc.g + 1 < total) load_q(next_item(sc.w));
+      }
+      advance(sc);
+    }
   };
 
   // K(0) must be resident before slot 0; the Q loads above land with it.
@@ -342,7 +487,8 @@ __device__ __forceinline__ void fwd_f16_block(const KernelParams& p, const WorkI
   // first read in slot 2t+4; it waits for them at the end of its next M phase
   // (slot 2t+3), before the barrier that closes that slot.  A wave works on
   // tiles t < wave_tiles only (causal waves above the diagonal stop early)
-  // but takes part in every slot's barrier.
+  // but takes part in every slot's barrier.  The stream runs the same slots,
+  // counted in stream steps instead of tiles.
   auto iteration = [&](int t, auto mwork, auto vwork) {
     wave_priority<1>();
     mwork();
@@ -361,12 +507,20 @@ __device__ __forceinline__ void fwd_f16_block(const KernelParams& p, const WorkI
     vwork();
     barrier();
   };
-  const int W = wave_tiles;
   if (group_b) {
     issue_k(1);
     issue_v(0);
     barrier();
   }
+  if constexpr (STREAM) {
+    iteration(0, [&] { m_s(0); }, [&] { v_phase(0); });
+    for (int g = 1; g < total; ++g) iteration(g, [&] { m_pv_s(g); }, [&] { v_phase(g); });
+    iteration(total, [&] { m_pv(total); }, [] {});
+    if (!group_b) barrier();
+    store(done);
+    return;
+  }
+  const int W = wave_tiles;
   iteration(
       0, [&] { if (W >= 1) m_s(0); }, [&] { if (W >= 1) v_phase(0); });
   for (int t = 1; t < W; ++t) iteration(t, [&] { m_pv_s(t); }, [&] { v_phase(t); });
@@ -391,410 +545,11 @@ __device__ __forceinline__ void fwd_f16_block(const KernelParams& p, const WorkI
   }
 }
 
-// The unmasked persistent schedule as one stream of tiles: a workgroup's items
-// (work items j0, j0 + stride, ..., R of them) run back to back through the
-// same two-group pipeline, so it fills and drains once per workgroup rather
-// than once per item, the next item's Q is loaded during the last softmax
-// phase of the current one, and the finished item's O is stored during the
-// first softmax phase of the next.  Each item's arithmetic is that of
-// fwd_f16_block (same products, same order), so O and LSE are bitwise equal.
-// Every wave computes every tile (rows past N are zeros and never stored).
-template <typename T, int D>
-__device__ __forceinline__ void fwd_f16_stream(const KernelParams& p, const int64_t j0,
-                                               const int64_t stride, const int R) {
-  constexpr bool CAUSAL = false;
-  using H = Half<T>;
-  using Frag = typename H::Frag;
-  using Pair = typename H::Pair;
-  using Sw = Swizzle<D>;
-  constexpr int NW = 8;              // waves per workgroup
-  constexpr int BR = NW * 32;        // query rows per workgroup
-  constexpr int BC = 128;            // keys per tile
-  constexpr int RB = D * 2;          // bytes per row of K or V
-  constexpr int CPR = D / 8;         // 16-byte chunks per row
-  constexpr int TILE = BC * RB;      // bytes of one staged K (or V) tile
-  constexpr int NKB = BC / 32;       // 32-key blocks per tile
-  constexpr int NKS = D / 16;        // MFMAs per 32x32 score block
-  constexpr int ND = D / 32;         // 32-row blocks of O^T
-  constexpr int RPL = 1024 / RB;     // rows one wave-wide 1 KiB load covers
-  constexpr int LPW = TILE / 1024 / 4;  // 1 KiB loads per loading wave per tensor
-  static_assert(LPW >= 1 && TILE % 4096 == 0, "tile shape");
-
-  __shared__ __attribute__((aligned(1024))) char smem[2][2][TILE];  // [K, V][buffer]
-
-  const int64_t N = p.N;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const bool group_b = wave >= 4;
-  const int gw = wave & 3;  // wave index inside its group
-  const int l32 = lane & 31;
-  const int hh = lane >> 5;
-  // Item r of this workgroup is work item j0 + r*stride (head-major).  Step g
-  // of the stream is tile g % n_tiles of item g / n_tiles.  Positions in the
-  // stream are tracked by cursors that advance one step at a time, so the
-  // loop divides nothing: the next item is the current one plus stride,
-  // split once into whole heads and query blocks.
-  const int n_tiles = (int)((N + BC - 1) / BC);  // tiles per item
-  const int total = R * n_tiles;                 // steps of the stream
-  // Wave-uniform values, pinned to scalar registers.
-  auto uniform64 = [](int64_t x) {
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
-    return (int64_t)(((uint64_t)hi << 32) | lo);
-  };
-  const int64_t s_bh = uniform64(stride / p.n_qblk);
-  const int s_qb = __builtin_amdgcn_readfirstlane((int)(stride % p.n_qblk));
-  auto next_item = [&](WorkItem w) {
-    w.bh += s_bh;
-    w.qblk += s_qb;
-    if (w.qblk >= p.n_qblk) {
-      w.qblk -= p.n_qblk;
-      w.bh += 1;
-    }
-    return w;
-  };
-  struct Cursor {
-    WorkItem w;  // item of the step
-    int t;       // tile of the step within the item
-    int g;       // step
-  };
-  WorkItem first;
-  first.bh = uniform64(j0 / p.n_qblk);
-  first.qblk = __builtin_amdgcn_readfirstlane((int)(j0 % p.n_qblk));
-  auto advance = [&](Cursor& cu) {
-    ++cu.g;
-    if (++cu.t == n_tiles) {
-      cu.t = 0;
-      cu.w = next_item(cu.w);
-    }
-  };
-  // Cursor of step cu.g + k (k >= 0), one item at a time.
-  auto ahead = [&](Cursor cu, int k) {
-    cu.g += k;
-    cu.t += k;
-    while (cu.t >= n_tiles) {
-      cu.t -= n_tiles;
-      cu.w = next_item(cu.w);
-    }
-    return cu;
-  };
-
-  // ---- tile loads: global -> LDS, 16 bytes per lane -------------------------
-  // Group B (four waves) loads every tile.  Load j of group-wave gw
-  // covers rows (gw*LPW + j)*RPL .. +RPL of the tile; lane i fills LDS chunk
-  // slot i%CPR of row .. + i/CPR, which holds global chunk slot ^ mask(row).
-  int kvoff[LPW], vvoff[LPW];
-#pragma unroll
-  for (int j = 0; j < LPW; ++j) {
-    const int r = (gw * LPW + j) * RPL + lane / CPR;
-    const int slot = lane % CPR;
-    kvoff[j] = r * RB + Sw::k(r, slot) * 16;
-    vvoff[j] = r * RB + Sw::v(r, slot) * 16;
-  }
-  const uint32_t lds_k = lds_addr(&smem[0][0][0]) + gw * LPW * 1024;
-  const uint32_t lds_v = lds_addr(&smem[1][0][0]) + gw * LPW * 1024;
-  // K and V tiles are issued in stream order, one step per call; the tile of
-  // step g goes to LDS buffer g % 2.
-  auto issue = [&](const void* base, uint32_t lds, const int* voffs, const Cursor cu) {
-    if (cu.g >= total) return;
-    const int64_t k0 = (int64_t)cu.t * BC;
-    const uint32_t rows = (uint32_t)(N - k0 < BC ? N - k0 : BC);
-    const u32x4 rs = buffer_rsrc((const T*)base + (cu.w.bh * N + k0) * D, rows * RB);
-#pragma unroll
-    for (int j = 0; j < LPW; ++j) dma_load16(rs, lds + (cu.g & 1) * TILE + j * 1024, voffs[j]);
-  };
-  // Step g's K and V, and the cursor sc of the next softmax phase: in the
-  // loop the V phase of step g issues K(g + 2) and V(g + 1).
-  Cursor sc{first, 0, 0};
-  auto issue_k = [&](int g) { issue(p.k, lds_k, kvoff, ahead(sc, g - sc.g)); };
-  auto issue_v = [&](int g) { issue(p.v, lds_v, vvoff, ahead(sc, g - sc.g)); };
-  auto barrier = [] {
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  auto wait_loads = [] {
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads have landed in LDS
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  // Q of item r (B operand of S^T = K Q^T): lane holds Q[qrow][16*ks + 8*hh
-  // .. +7] of its row qrow in the item's block (zeros past N).
-  // Loaded through a buffer resource that ends at row N (rows past it read as
-  // zeros), so that nothing waits for the data before the products that use
-  // it; only a negative scale (a sign flip of Q) reads it at once.
-  Frag qf[NKS];
-  auto load_q = [&](const WorkItem w) {
-    const int64_t q0 = (int64_t)w.qblk * BR;
-    const int64_t rows = N - q0 < BR ? N - q0 : BR;
-    const auto rs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((const T*)p.q + (w.bh * N + q0) * D), (short)0, (int)(rows * RB), 0x00020000);
-    const int off = (wave * 32 + l32) * RB + hh * 16;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-      qf[ks] = bits<Frag>(__builtin_amdgcn_raw_buffer_load_b128(rs, off, 32 * ks, 0));
-    if (p.q_sign) {
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) qf[ks] = bits<Frag>(bits<u32x4>(qf[ks]) ^ p.q_sign);
-    }
-  };
-  load_q(first);
-  if (group_b) issue_k(0);
-
-  // ---- lane-constant LDS read offsets ----------------------------------------
-  // K A operand for MFMA ks of key block kb: row kb*32 + krow, chunk 2*ks + hh
-  // (the swizzle only sees the row modulo 16, so kb does not change it).
-  const int krow = k_row_of_lane(l32);
-  int koff[NKS];
-#pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) koff[ks] = krow * RB + Sw::k(krow, 2 * ks + hh) * 16;
-  // V^T A operand for O^T block db, keys kb*32 + 16*jj + 8*hh + 4*t + 0..3:
-  // lane j of 16-lane group g addresses row (.. + j/4) at columns
-  // db*32 + 16*(g%2) + 4*(j%4); the swizzle only sees the row modulo 4.
-  int voff[ND];
-  {
-    const int g = lane >> 4, j16 = lane & 15;
-    const int vrow = 8 * hh + (j16 >> 2);
-#pragma unroll
-    for (int db = 0; db < ND; ++db) {
-      const int dcol = db * 32 + 16 * (g & 1) + 4 * (j16 & 3);
-      voff[db] = vrow * RB + Sw::v(vrow, dcol >> 3) * 16 + (dcol & 7) * 2;
-    }
-  }
-
-  // ---- running state ----------------------------------------------------------
-  f32x16 o[ND];
-#pragma unroll
-  for (int db = 0; db < ND; ++db) o[db] = f32x16{};
-  f32x16 s[NKB];
-  Frag pf[NKB][2];
-  float m = kNegInf;  // reference maximum of the row, log2 units
-  // This lane's share of the row sum (the keys it holds), accumulated on the
-  // matrix pipe next to the P V products of the same weights; element 0 is
-  // used (the product writes the same value to all four).
-  f32x4 lacc = f32x4{};
-  const float c = p.c;
-
-  // Epilogue of item w: O = O_acc / l, written once; LSE = (m + log2 l) * ln 2.
-  auto store = [&](const WorkItem w) {
-    const int64_t qrow = (int64_t)w.qblk * BR + (int64_t)wave * 32 + l32;
-    const float lt = halves_sum(lacc[0]);
-    if (qrow < N) {
-      const float inv = 1.0f / lt;
-      if (hh == 0) p.lse[w.bh * N + qrow] = (m + __builtin_amdgcn_logf(lt)) * kLn2;
-      T* dst = (T*)p.o + (w.bh * N + qrow) * D + hh * 4;
-#pragma unroll
-      for (int db = 0; db < ND; ++db)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const Pair lo = H::pack(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
-          const Pair hi = H::pack(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
-          *(u32x2*)(dst + db * 32 + g * 8) = u32x2{bits<uint32_t>(lo), bits<uint32_t>(hi)};
-        }
-    }
-  };
-
-  // M phase of tile t: O += P(t-1) V(t-1), then S(t) = K(t) Q^T: NPV + NS
-  // matrix products whose A operands come from LDS.  In the steady state
-  // (m_pv_s) the operand reads run kPipe products ahead of the products, so
-  // LDS latency hides under the matrix pipe; the sched_group_barrier pairs
-  // pin that order.  The stream's first step has no P V product and its
-  // last (g = total) no score product (m_s, m_pv).
-  constexpr int NPV = NKB * 2 * ND;  // O^T += V^T P^T products
-  constexpr int NS = NKS * NKB;      // S^T = K Q^T products
-  constexpr int kPipe = 3;
-  auto fetch = [&](const char* vl, const char* kl, int i) -> Frag {
-    if (i < NPV) {
-      const int kb = i / (2 * ND), jj = (i / ND) % 2, db = i % ND;
-      const int off = (kb * 32 + 16 * jj) * RB + voff[db];
-      const u32x2 lo = lds_read_tr(vl, off);
-      const u32x2 hi = lds_read_tr(vl, off + 4 * RB);
-      return bits<Frag>(u32x4{lo[0], lo[1], hi[0], hi[1]});
-    }
-    const int j = i - NPV, ks = j / NKB, kb = j % NKB;
-    return bits<Frag>(*(const u32x4*)(kl + kb * 32 * RB + koff[ks]));
-  };
-  auto apply = [&](int i, Frag a) {
-    if (i < NPV) {
-      const int kb = i / (2 * ND), jj = (i / ND) % 2, db = i % ND;
-      o[db] = H::mma(a, pf[kb][jj], o[db]);
-      if (db == ND - 1) {
-        const u32x4 w = bits<u32x4>(pf[kb][jj]);
-        lacc = H::sum4(u32x2{w[0], w[1]}, lacc);
-        lacc = H::sum4(u32x2{w[2], w[3]}, lacc);
-      }
-    } else {
-      const int j = i - NPV, ks = j / NKB, kb = j % NKB;
-      s[kb] = H::mma(a, qf[ks], s[kb]);
-    }
-  };
-  auto m_pv_s = [&](int t) {
-    const char* vl = &smem[1][(t - 1) & 1][0];
-    const char* kl = &smem[0][t & 1][0];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
-    Frag ring[kPipe];
-    constexpr int PRE = 2 * kPipe;  // the first kPipe products are P V products
-    static_assert(kPipe <= NPV, "pipeline prologue");
-#pragma unroll
-    for (int i = 0; i < kPipe; ++i) ring[i] = fetch(vl, kl, i);
-    __builtin_amdgcn_sched_group_barrier(0x100, PRE, 0);
-#pragma unroll
-    for (int i = 0; i < NPV + NS; ++i) {
-      const Frag a = ring[i % kPipe];
-      if (i + kPipe < NPV + NS) ring[i % kPipe] = fetch(vl, kl, i + kPipe);
-      apply(i, a);
-      if (i + kPipe < NPV + NS) {
-        if (i + kPipe < NPV) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        } else {
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
-      }
-      if (i < NPV && i % ND == ND - 1) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);  // with the two row-sum products
-      } else {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      }
-    }
-  };
-  auto m_pv = [&](int t) {
-    const char* vl = &smem[1][(t - 1) & 1][0];
-#pragma unroll
-    for (int i = 0; i < NPV; ++i) apply(i, fetch(vl, vl, i));
-  };
-  auto m_s = [&](int t) {
-    const char* kl = &smem[0][t & 1][0];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
-#pragma unroll
-    for (int i = NPV; i < NPV + NS; ++i) apply(i, fetch(kl, kl, i));
-  };
-
-  // V phase of step g: online softmax of S(g) into P(g).  The first step of
-  // an item first stores the previous item (its last P V product ran in the
-  // M phase just before) and starts the running state afresh; the last step
-  // of an item loads the next item's Q (the last product that reads Q ran in
-  // the M phase just before).
-  WorkItem done = first;   // item before sc's item (valid once sc.g >= n_tiles)
-  auto v_phase = [&](int) {
-    const int t = sc.t;
-    if (t == 0 && sc.g > 0) {
-      store(done);
-#pragma unroll
-      for (int db = 0; db < ND; ++db) o[db] = f32x16{};
-      lacc = f32x4{};
-      m = kNegInf;
-    }
-    const int64_t k0 = (int64_t)t * BC;
-    // Keys k0 + i with i >= lim are past N: their scores become -inf.
-    // Register r of key block kb holds key kb*32 + key_of_reg(r, hh) of the
-    // tile.
-    const int64_t lim64 = N - k0;
-    const bool need_mask = k0 + BC > N;
-    if (need_mask) {
-      const int lim = (int)(lim64 < 0 ? 0 : (lim64 > BC ? BC : lim64)) - 8 * hh;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (kb * 32 + key_of_reg(r, 0) >= lim) s[kb][r] = kNegInf;
-    }
-    // Row maximum as a tree (short dependency chains), then across halves.
-    float mx = chain_max4<NKB * 16>([&](int i) { return s[i / 16][i % 16]; });
-    mx = halves_max(mx);
-    const float mxc = mx * c;  // c > 0, so -inf stays -inf
-
-    // Online softmax: raise the reference maximum (and rescale l and O by
-    // exp2(m_old - m_new)) only when this tile exceeds it by the slack.
-    // m = -inf means no visible key yet: any visible key raises it.
-    const bool grow = mxc > m + kRescaleSlack;
-    if (__ballot(grow)) {
-      const float alpha = grow ? __builtin_amdgcn_exp2f(m - mxc) : 1.0f;
-      m = grow ? mxc : m;
-      lacc *= alpha;
-#pragma unroll
-      for (int db = 0; db < ND; ++db) o[db] *= alpha;
-    }
-    // A lane whose row has seen no visible key yet keeps m = -inf; its
-    // weights are exp2(-inf) = 0 either way.
-    const float m_use = m == kNegInf ? 0.f : m;
-
-    // P = exp2(c*s - m), rounded to T (the row sum is formed from these
-    // rounded weights in the next matrix phase, so O's normalisation matches
-    // the weights P V actually uses).  Masked scores are -inf and c > 0, so
-    // their weight is exp2(-inf) = 0.
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        u32x4 f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * jj + 2 * i], c, -m_use));
-          const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * jj + 2 * i + 1], c, -m_use));
-          f[i] = bits<uint32_t>(H::pack(e0, e1));
-        }
-        pf[kb][jj] = bits<Frag>(f);
-      }
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) fence(pf[kb][jj]);
-    fence(lacc);
-    fence(m);
-    if (t == n_tiles - 1) {
-      done = sc.w;
-      if (sc.g + 1 < total) load_q(next_item(sc.w));
-    }
-    advance(sc);
-  };
-
-  // K(0) of the first item must be resident before slot 0; the Q loads above
-  // land with it.
-  wait_loads();
-  barrier();
-
-  // Slots as in fwd_f16_block, counted in stream steps g instead of tiles:
-  // group B runs one slot behind group A and issues K(g+2) and V(g+1) at the
-  // start of its V phase of step g.
-  auto iteration = [&](int t, auto mwork, auto vwork) {
-    wave_priority<1>();
-    mwork();
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) fence(s[kb]);
-#pragma unroll
-    for (int db = 0; db < ND; ++db) fence(o[db]);
-    fence(lacc);
-    wave_priority<0>();
-    if (group_b) wait_loads();
-    barrier();
-    if (group_b) {
-      issue_k(t + 2);
-      issue_v(t + 1);
-    }
-    vwork();
-    barrier();
-  };
-  if (group_b) {
-    issue_k(1);
-    issue_v(0);
-    barrier();
-  }
-  iteration(0, [&] { m_s(0); }, [&] { v_phase(0); });
-  for (int g = 1; g < total; ++g) iteration(g, [&] { m_pv_s(g); }, [&] { v_phase(g); });
-  iteration(total, [&] { m_pv(total); }, [] {});
-  if (!group_b) barrier();
-  store(done);
-}
-
 // One workgroup per 256-row block; the hardware dispatcher hands the blocks
 // to CUs in the order of work_item (longest first when causal).
 template <typename T, int D, bool CAUSAL>
 __global__ void __launch_bounds__(512, 1) fwd_f16_kernel(KernelParams p) {
-  fwd_f16_block<T, D, CAUSAL>(p, work_item<CAUSAL>(p.n_qblk));
+  fwd_f16_tiles<T, D, CAUSAL, false>(p, work_item<CAUSAL>(p.n_qblk), 0, 0, 1);
 }
 
 // Persistent schedule ("FlashAttention Evolution", FA-4 card: persistent
@@ -814,7 +569,7 @@ __global__ void __launch_bounds__(512, 1) fwd_f16_persistent_kernel(KernelParams
   if constexpr (!CAUSAL) {
     // Items gx, gx + G, gx + 2G, ... as one tile stream.
     const int R = gx < p.n_items ? (int)((p.n_items - gx + G - 1) / G) : 0;
-    if (R > 0) fwd_f16_stream<T, D>(p, gx, G, R);
+    if (R > 0) fwd_f16_tiles<T, D, false, true>(p, WorkItem{}, gx, G, R);
     return;
   }
   const int64_t n_bh = p.n_items / p.n_qblk;
@@ -829,7 +584,7 @@ __global__ void __launch_bounds__(512, 1) fwd_f16_persistent_kernel(KernelParams
       wi.bh = j / p.n_qblk;
       wi.qblk = (int)(j % p.n_qblk);
     }
-    fwd_f16_block<T, D, CAUSAL>(p, wi);
+    fwd_f16_tiles<T, D, CAUSAL, false>(p, wi, 0, 0, 1);
   }
 }
 
