@@ -247,3 +247,38 @@ def test_many_unmasked_blocks(dtype, d, N, heads, scale):
     rows = np.broadcast_to(rows, (B, H, rows.size))
     check(o, lse, q, k, v, scale, False, dtype, rows=rows,
           label=f"{dtype} d={d} N={N} B*H={heads} scale={scale:.3f}")
+
+
+@pytest.mark.parametrize("B,H,N,causal", [
+    (1, 3, 700, True),      # one workgroup per block (the grid)
+    (2, 16, 4096, False),   # two blocks per CU: the persistent tile stream
+])
+def test_graph_capture_replays(B, H, N, causal):
+    """flash_attn_fwd enqueues one kernel, allocates nothing and clears no
+    memory, so it can be captured in a HIP graph: three replays, with eager
+    work on other tensors between them, each bitwise equal to the eager call."""
+    q, k, v = (x.to(DEV) for x in W.random_qkv(B, H, N, 128, "f16", seed=9100 + N))
+    scale = W.default_scale(128)
+    o_ref, lse_ref = gpu_forward(q, k, v, scale, causal)
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, N, dtype=torch.float32, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up call on the capture stream
+        flash_attn_fwd(q, k, v, o, lse, scale=scale, causal=causal)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        flash_attn_fwd(q, k, v, o, lse, scale=scale, causal=causal)
+    for rep in range(3):
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(lse, lse_ref), f"replay {rep}"
+        # unrelated eager work between replays
+        o2, _ = gpu_forward(q[:, :1].contiguous(), k[:, :1].contiguous(), v[:, :1].contiguous(),
+                            scale, causal)
+        assert torch.equal(o2, o_ref[:, :1])
