@@ -23,7 +23,8 @@
 //     O += P(t-1) V(t-1) followed by S(t) = K(t) Q^T, and its V phase turns
 //     S(t) into P(t).  (On gfx950 a 32x32x16 MFMA blocks its SIMD's vector
 //     issue for most of its 32 cycles, so ordinary vector work barely hides
-//     under matrix work; the alternation gives each phase whole slots.)
+//     under matrix work; the alternation gives each phase whole slots.)  The
+//     wave in its M phase runs at issue priority 1, its partner at 0.
 //   * K and V tiles (128 keys) are double buffered in LDS and filled by
 //     buffer_load ... lds (HBM/L2 straight into LDS, no register staging),
 //     issued by the group entering its V phase.  Each row's 16-byte chunks
@@ -33,12 +34,14 @@
 //     ahead and only waited for at the barrier before their first use.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_{f16,bf16}: a lane owns one query
 //     (accumulator column) and 16 keys of each 32-key block, the other 16 sit
-//     in lane l^32, so the row max and sum are in-lane plus one
-//     v_permlane32_swap, and the rescale factor is a per-lane scalar.  Q stays
-//     in registers for the whole loop.
+//     in lane l^32, so the row max is in-lane plus one v_permlane32_swap,
+//     and the rescale factor is a per-lane scalar.  Q stays in registers for
+//     the whole loop.
 //   * O^T += V^T P^T: P^T is the B operand taken straight from the score
 //     registers (rounded to the input type), V^T comes from row-major V in
-//     LDS through ds_read_b64_tr_b16 transposing loads.
+//     LDS through ds_read_b64_tr_b16 transposing loads.  The row sum of the
+//     rounded weights is formed next to these products on the matrix pipe
+//     (4x4x4 products against an all-ones operand), not on the vector ALU.
 //   * exp is exp2 with log2(e) folded into the scale.  The reference maximum
 //     is only raised when a tile's maximum exceeds it by more than
 //     kRescaleSlack (log2 units); until then the weights are exp2 of at most
@@ -561,7 +564,8 @@ __global__ void __launch_bounds__(512, 1) fwd_f16_kernel(KernelParams p) {
 // a workgroup all share one residue of (b*H + h) mod 8 per round parity, so
 // an XCD (workgroup g runs on XCD g % 8) keeps to a few heads.  Unmasked items
 // are equal in cost: workgroup g of XCD x takes a contiguous range of items
-// per round, head-major, so a head's blocks share that XCD's L2.
+// per round, head-major, so a head's blocks share that XCD's L2, and runs its
+// items as one tile stream (fwd_f16_tiles with STREAM).
 template <typename T, int D, bool CAUSAL>
 __global__ void __launch_bounds__(512, 1) fwd_f16_persistent_kernel(KernelParams p) {
   const int G = gridDim.x, g = blockIdx.x;
