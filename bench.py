@@ -60,6 +60,9 @@ KERNEL_NAME_PATTERN = {"f16": ("fwd_f16_", "fwd_f16_"),
 PROFILES = os.path.join(ROOT, "profiles")
 COPY_BYTES = 512 << 20  # one calibration copy: 512 MiB read + 512 MiB written
 COPY_REPS = 3
+SETTLE_S = 1.5  # untimed calls before the warm-up steps, while the clock ramps from idle
+DIST_S = 1.0  # the per-call timing window after the timed region (clock sampled there)
+MIN_CLOCK_SAMPLES = 10
 
 
 def kernel_source_digest(key: str) -> str:
@@ -110,52 +113,89 @@ def measured_traffic(workload: str, key: str):
     return float(val.group(1))
 
 
+def host_cpu():
+    """(cores this process may use, CPU model name)."""
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # non-Linux
+        cores = os.cpu_count() or 1
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return cores, model
+
+
+def run_oracle_pool(units, run_unit, budget_s: float):
+    """Runs run_unit(u) for the units in order on a pool of threads, one per
+    core (at most 16), each with one BLAS thread: numpy releases the
+    interpreter lock inside its array loops and BLAS products, so the units
+    run in parallel.  New units are started until budget_s has passed (at
+    least one).  Returns (sum of what the finished units returned, their
+    count, elapsed seconds, threads)."""
+    from concurrent.futures import FIRST_COMPLETED, ThreadPoolExecutor, wait
+
+    from threadpoolctl import threadpool_limits
+    cores, _ = host_cpu()
+    workers = max(1, min(cores, 16))
+    total, count = 0.0, 0
+    it = iter(units)
+    t0 = time.perf_counter()
+    with threadpool_limits(1), ThreadPoolExecutor(workers) as ex:
+        pending, exhausted = set(), False
+        while True:
+            while (not exhausted and len(pending) < 2 * workers
+                   and (count + len(pending) == 0 or time.perf_counter() - t0 < budget_s)):
+                u = next(it, None)
+                if u is None:
+                    exhausted = True
+                    break
+                pending.add(ex.submit(run_unit, u))
+            if not pending:
+                break
+            done, pending = wait(pending, return_when=FIRST_COMPLETED)
+            for f in done:
+                total += f.result()
+                count += 1
+    return total, count, time.perf_counter() - t0, workers
+
+
+def _baseline_record(value, unit, workers, sample):
+    cores, model = host_cpu()
+    return {"value": value, "unit": unit, "cores": workers, "kind": "oracle", "sample": sample,
+            "host_cores": cores, "cpu_model": model}
+
+
 def cpu_baseline(w, q, k, v, budget_s: float):
-    """Times the fp64 oracle on the workload's own inputs, one block of 512
-    query rows at a time (heads in order, rows in order), until the budget is
-    spent; at least one block.  FLOPs are counted per row from the number of
-    keys the row sees (4*d per visible key)."""
+    """Times the fp64 oracle on the workload's own inputs in blocks of 512
+    query rows (heads in order, rows in order) on a thread pool over the host's
+    cores, starting blocks until the budget is spent.  FLOPs are counted per
+    row from the number of keys the row sees (4*d per visible key)."""
     import numpy as np
 
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()
-                       if p.get("user_api") == "blas"] or [1])
-    except Exception:  # threadpoolctl missing: numpy's BLAS default
-        threads = len(os.sched_getaffinity(0))
     block = 512
-    rows_done = heads_touched = 0
-    flops = 0.0
-    t0 = time.perf_counter()
-    done = False
-    for b in range(w.B):
-        for h in range(w.H):
-            sl = (slice(b, b + 1), slice(h, h + 1))
-            heads_touched += 1
-            for r0 in range(0, w.N, block):
-                idx = np.arange(r0, min(r0 + block, w.N), dtype=np.int64)
-                oracle.attention_forward(q[sl], k[sl], v[sl], w.scale, w.causal, rows=idx)
-                visible = (idx + 1) if w.causal else np.full(idx.shape, w.N)
-                flops += 4.0 * w.d * float(visible.sum())
-                rows_done += len(idx)
-                if time.perf_counter() - t0 >= budget_s:
-                    done = True
-                    break
-            if done:
-                break
-        if done:
-            break
-    el = time.perf_counter() - t0
-    total_rows = w.B * w.H * w.N
-    return {
-        "value": flops / el / 1e12,
-        "unit": "TFLOP/s",
-        "cores": threads,
-        "kind": "oracle",
-        "sample": f"{rows_done} of {total_rows} query rows of {w.name} (first {heads_touched} "
-                  f"(b,h) heads, rows in order, blocks of {block}), fp64 numpy, {el:.1f} s",
-    }
+    units = [(b, h, r0) for b in range(w.B) for h in range(w.H) for r0 in range(0, w.N, block)]
+
+    def run(u):
+        b, h, r0 = u
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        idx = np.arange(r0, min(r0 + block, w.N), dtype=np.int64)
+        oracle.attention_forward(q[sl], k[sl], v[sl], w.scale, w.causal, rows=idx)
+        visible = (idx + 1) if w.causal else np.full(idx.shape, w.N)
+        return 4.0 * w.d * float(visible.sum())
+
+    flops, n, el, workers = run_oracle_pool(units, run, budget_s)
+    rows_done = sum(min(block, w.N - units[i][2]) for i in range(n))
+    return _baseline_record(
+        flops / el / 1e12, "TFLOP/s", workers,
+        f"{rows_done} of {w.B * w.H * w.N} query rows of {w.name} (the first {n} blocks of "
+        f"{block} rows, heads in order), fp64 numpy, {workers} threads, {el:.1f} s")
 
 
 def _counter_rows(path, counter):
@@ -241,10 +281,11 @@ def percentile(sorted_vals, f):
 
 class ClockSampler:
     """Samples the GPU's graphics clock (MHz) through amdsmi in a background
-    thread.  Reading the clock changes no setting; when amdsmi is missing or
-    refuses, no samples are taken and the clock fields are left out."""
+    thread, with the time of each sample.  Reading the clock changes no
+    setting; when amdsmi is missing or refuses, no samples are taken and the
+    clock fields are left out."""
 
-    def __init__(self, period_s=0.02):
+    def __init__(self, period_s=0.01):
         self.period_s = period_s
         self.samples = []
         self._stop = None
@@ -287,7 +328,7 @@ class ClockSampler:
                 except Exception:
                     return
                 if x:
-                    self.samples.append(x)
+                    self.samples.append((time.perf_counter(), x))
                 self._stop.wait(self.period_s)
 
         self._thread = threading.Thread(target=run, daemon=True)
@@ -303,78 +344,51 @@ class ClockSampler:
         except Exception:
             pass
 
-    def median_mhz(self):
-        if not self.samples:
-            return None
-        v = sorted(self.samples)
-        return v[len(v) // 2]
+    def window(self, t0, t1):
+        """Samples taken between perf_counter times t0 and t1."""
+        return [x for t, x in self.samples if t0 <= t <= t1]
 
 
 def cpu_baseline_cache(w, q, k, v, budget_s: float):
-    """Times the fp64 oracle on a key/value-cache workload, one (b, h) head at
-    a time until the budget is spent (at least one head); the rate is the
-    compulsory bytes of the heads done per second, like the GPU figure."""
+    """Times the fp64 oracle on a key/value-cache workload, whole (b, h) heads
+    on a thread pool over the host's cores until the budget is spent; the rate
+    is the compulsory bytes of the heads done per second, like the GPU figure."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()
-                       if p.get("user_api") == "blas"] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
-    heads = 0
-    t0 = time.perf_counter()
-    for b in range(w.B):
-        for h in range(w.H):
-            sl = (slice(b, b + 1), slice(h, h + 1))
-            oracle.attention_forward(q[sl], k[sl], v[sl], w.scale, w.causal)
-            heads += 1
-            if time.perf_counter() - t0 >= budget_s:
-                break
-        else:
-            continue
-        break
-    el = time.perf_counter() - t0
-    done_bytes = w.compulsory_bytes() * heads / (w.B * w.H)
-    return {
-        "value": done_bytes / el / 1e9,
-        "unit": "GB/s",
-        "cores": threads,
-        "kind": "oracle",
-        "sample": f"{heads} of {w.B * w.H} (b,h) heads of {w.name}, all {w.Nq} query rows "
-                  f"each, fp64 numpy, {el:.1f} s",
-    }
+    per_head = w.compulsory_bytes() / (w.B * w.H)
+
+    def run(u):
+        b, h = u
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        oracle.attention_forward(q[sl], k[sl], v[sl], w.scale, w.causal)
+        return per_head
+
+    done_bytes, heads, el, workers = run_oracle_pool(
+        [(b, h) for b in range(w.B) for h in range(w.H)], run, budget_s)
+    return _baseline_record(
+        done_bytes / el / 1e9, "GB/s", workers,
+        f"{heads} of {w.B * w.H} (b,h) heads of {w.name}, all {w.Nq} query rows each, "
+        f"fp64 numpy, {workers} threads, {el:.1f} s")
 
 
 def cpu_baseline_bwd(w, q, k, v, do, budget_s: float):
-    """Times the fp64 backward oracle one (b, h) head at a time until the
-    budget is spent (at least one head); FLOPs as the workload counts them."""
+    """Times the fp64 backward oracle, whole (b, h) heads on a thread pool
+    over the host's cores until the budget is spent; FLOPs as the workload
+    counts them."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()
-                       if p.get("user_api") == "blas"] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
-    heads = 0
-    t0 = time.perf_counter()
-    for b in range(w.B):
-        for h in range(w.H):
-            sl = (slice(b, b + 1), slice(h, h + 1))
-            oracle.attention_backward(q[sl], k[sl], v[sl], do[sl], w.scale, w.causal)
-            heads += 1
-            if time.perf_counter() - t0 >= budget_s:
-                break
-        else:
-            continue
-        break
-    el = time.perf_counter() - t0
-    return {
-        "value": w.flops() * heads / (w.B * w.H) / el / 1e12,
-        "unit": "TFLOP/s",
-        "cores": threads,
-        "kind": "oracle",
-        "sample": f"{heads} of {w.B * w.H} (b,h) heads of {w.name}, whole heads, fp64 numpy, {el:.1f} s",
-    }
+    per_head = w.flops() / (w.B * w.H)
+
+    def run(u):
+        b, h = u
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        oracle.attention_backward(q[sl], k[sl], v[sl], do[sl], w.scale, w.causal)
+        return per_head
+
+    flops, heads, el, workers = run_oracle_pool(
+        [(b, h) for b in range(w.B) for h in range(w.H)], run, budget_s)
+    return _baseline_record(
+        flops / el / 1e12, "TFLOP/s", workers,
+        f"{heads} of {w.B * w.H} (b,h) heads of {w.name}, whole heads, fp64 numpy, "
+        f"{workers} threads, {el:.1f} s")
 
 
 def main():
@@ -382,8 +396,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=None,
-                    help="untimed warm-up steps (default: as many as fill 1.5 s, at least 10, so the "
-                         "GPU clocks reach their loaded steady state)")
+                    help="untimed warm-up steps (default 10), after 1.5 s of untimed calls that "
+                         "let the GPU clock reach its loaded steady state")
+    ap.add_argument("--settle", type=float, default=SETTLE_S,
+                    help="seconds of untimed calls before the warm-up steps (clock settling)")
     ap.add_argument("--workload", default=None)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle time for cpu_baseline (0 = skip)")
@@ -475,18 +491,23 @@ def main():
         def step():
             flash_attn_fwd(qd, kd, vd, o, lse, scale=w.scale, causal=w.causal, stream=stream)
 
-    if args.warmup is None:
-        warmup = 0
-        t_w = time.perf_counter()
-        while warmup < 10 or time.perf_counter() - t_w < 1.5:
-            for _ in range(10):
-                step()
-            warmup += 10
-            torch.cuda.synchronize()
-    else:
-        warmup = args.warmup
-        for _ in range(warmup):
+    clock = ClockSampler()
+    clock.start()
+    # Clock settling, before the warm-up steps: the card starts from its idle
+    # clock and takes about a second of sustained load to reach the clock it
+    # holds under this kernel (power-limited, below the 2.4 GHz peak).  These
+    # calls are untimed and reported in the JSON line as "clock_settle".
+    settle_calls = 0
+    t_s = time.perf_counter()
+    while time.perf_counter() - t_s < args.settle:
+        for _ in range(10):
             step()
+        settle_calls += 10
+        torch.cuda.synchronize()
+    settle_s = time.perf_counter() - t_s
+    warmup = 10 if args.warmup is None else args.warmup
+    for _ in range(warmup):
+        step()
     torch.cuda.synchronize()
     # HIP events recorded on the stream the kernels are launched on.
     start = torch.cuda.Event(enable_timing=True)
@@ -500,21 +521,28 @@ def main():
     wall = time.perf_counter() - t0
     ms = start.elapsed_time(end) / args.steps  # one call per step
 
-    # Per-call distribution: one event pair around each call, after the timed
-    # region (so the extra event records do not perturb it), with the
-    # graphics clock sampled meanwhile.
-    n_dist = min(args.steps, max(20, int(2.0 / max(ms * 1e-3, 1e-6))))
+    # Per-call distribution: one event pair around each call (at most 2000)
+    # after the timed region, so the extra event records do not perturb it;
+    # calls continue for at least DIST_S so that the graphics clock, sampled
+    # every 10 ms, is read over a window of this kernel's sustained load.
+    n_dist = min(2000, max(20, int(DIST_S / max(ms * 1e-3, 1e-6))))
     pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
              for _ in range(n_dist)]
-    clock = ClockSampler()
-    clock.start()
+    t_d = time.perf_counter()
     for a, b in pairs:
         a.record(stream)
         step()
         b.record(stream)
     torch.cuda.synchronize()
+    while time.perf_counter() - t_d < DIST_S:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+    t_d_end = time.perf_counter()
     clock.stop()
     per_launch = sorted(a.elapsed_time(b) for a, b in pairs)
+    clk = sorted(clock.window(t_d, t_d_end))
+    mhz = clk[len(clk) // 2] if len(clk) >= MIN_CLOCK_SAMPLES else None
 
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -532,7 +560,6 @@ def main():
     traffic = measured_traffic(name, key) if args.persistent is None else None
     dist = [round(percentile(per_launch, f), 5) for f in (0.1, 0.5, 0.9)]
     props = torch.cuda.get_device_properties(dev)
-    mhz = clock.median_mhz()
     if cache:
         # Reading the cache from HBM bounds this path: GB/s against HBM peak.
         roofline = {
@@ -552,6 +579,7 @@ def main():
         }
         if mhz:
             roofline["gfx_clock_mhz_median"] = round(mhz, 1)
+            roofline["clock_samples"] = len(clk)
         result = {
             "metric": "attention decode against a K/V cache: GB/s of compulsory HBM bytes (1 GPU)",
             "value": round(gbps, 1),
@@ -586,9 +614,15 @@ def main():
             "launches_sampled": len(per_launch),
         }
         if mhz:
-            # The same kernel against the peak at the clock the card actually ran.
+            # The per-call median against the peak at the clock the card ran
+            # during those same calls.  A fraction above 1 would mean the
+            # clock reading does not describe the kernel's calls: then it is
+            # left out.
             roofline["gfx_clock_mhz_median"] = round(mhz, 1)
-            roofline["frac_at_measured_clock"] = round(tflops / (peak * mhz / PEAK_CLOCK_MHZ), 4)
+            roofline["clock_samples"] = len(clk)
+            f = flops / (dist[1] * 1e-3) / 1e12 / (peak * mhz / PEAK_CLOCK_MHZ)
+            if 0 < f <= 1:
+                roofline["frac_at_measured_clock"] = round(f, 4)
         result = {
             "metric": ("attention fwd TFLOP/s and % of MFMA peak, e4m3 inputs (1 GPU)" if key == "fp8"
                        else "attention bwd TFLOP/s (2.5x the forward's FLOPs) and % of MFMA peak (1 GPU)"
@@ -615,6 +649,8 @@ def main():
     result["device"] = {"name": props.name, "cus": props.multi_processor_count,
                         "arch": getattr(props, "gcnArchName", "")}
     result["timed_wall_s"] = round(wall, 4)
+    result["clock_settle"] = {"seconds": round(settle_s, 2), "calls": settle_calls,
+                              "note": "untimed calls before the warm-up steps"}
     if args.cpu_budget > 0:
         if cache:
             result["cpu_baseline"] = cpu_baseline_cache(w, q, k, v, args.cpu_budget)

@@ -308,7 +308,11 @@ fa_status flash_attn_bwd(const void* q, const void* k, const void* v, const void
       BH * N > (int64_t)UINT32_MAX / 16)
     return fail(FA_ERR_SHAPE, "B*H*ceil(N/%d) = %lld workgroups exceeds the grid limit",
                 fa::kBwdRowsPerWorkgroup, (long long)(BH * n_blk));
-  const int64_t need = BH * N * 4;
+  // D and LSE * log2(e) for every row (flash_attn_bwd_workspace_size): the
+  // prep kernel writes both halves, so the whole size is required and the
+  // whole range takes part in the overlap checks.
+  const int64_t need = flash_attn_bwd_workspace_size(B, H, N);
+  if (need <= 0) return fail(FA_ERR_SHAPE, "B*H*N overflows the workspace size");
   if (!workspace) return fail(FA_ERR_WORKSPACE, "the backward pass needs a workspace of %lld bytes", (long long)need);
   if ((uintptr_t)workspace & 15u) return fail(FA_ERR_ALIGN, "workspace must be 16-byte aligned");
   if (workspace_bytes < need)

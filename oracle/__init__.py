@@ -7,11 +7,13 @@ from .attention import (as_f64, attention_backward, attention_backward_sampled,
                         attention_forward, attention_partial,
                         backward_error_bound,
                         boundary_scale, causal_offset, decode_e4m3, dequantize_fp8,
-                        fp8_weight_error_bound, merge_partials, split_attention,
-                        streaming_attention)
+                        forward_error_bound_16, fp8_weight_error_bound,
+                        merge_partials, split_attention, streaming_attention,
+                        weight_rounding_error_bound, ROUNDING_16)
 
 __all__ = ["as_f64", "attention_backward", "attention_backward_sampled", "attention_forward",
            "attention_partial",
            "backward_error_bound", "boundary_scale",
-           "causal_offset", "decode_e4m3", "dequantize_fp8", "fp8_weight_error_bound",
-           "merge_partials", "split_attention", "streaming_attention"]
+           "causal_offset", "decode_e4m3", "dequantize_fp8", "forward_error_bound_16",
+           "fp8_weight_error_bound", "merge_partials", "split_attention",
+           "streaming_attention", "weight_rounding_error_bound", "ROUNDING_16"]

@@ -66,7 +66,10 @@ The later functions carry their derivations in their docstrings and are pinned
 in their own files: ``decode_e4m3``, ``dequantize_fp8`` and
 ``fp8_weight_error_bound`` (tests/test_oracle_fp8.py: every e4m3 code against
 torch's float8_e4m3fn, fixed values, simulated weight rounding inside the
-bound); ``attention_backward`` and
+bound); ``weight_rounding_error_bound`` with 16-bit parameters and
+``forward_error_bound_16`` (tests/test_oracle_bound16.py: a float64 simulation
+of the 16-bit roundings stays inside the bound and reaches a good part of it);
+``attention_backward`` and
 ``backward_error_bound`` (tests/test_oracle_backward.py: torch autograd and
 SDPA in float64, central finite differences of ``attention_forward``,
 invariants, planted mistakes, simulated 16-bit rounding inside the bound);
@@ -304,15 +307,31 @@ def dequantize_fp8(x, descale: float) -> np.ndarray:
 def fp8_weight_error_bound(q, k, v, scale: float, causal: bool = False, rows=None,
                            u: float = 2.0 ** -4, a: float = 2.0 ** -10
                            ) -> Tuple[np.ndarray, np.ndarray]:
+    """``weight_rounding_error_bound`` for weights rounded to e4m3: half a unit
+    in the last place is relative 2^-4 in the normal range and absolute 2^-10
+    below 2^-6 (subnormals, spacing 2^-9)."""
+    return weight_rounding_error_bound(q, k, v, scale, causal, rows, u, a)
+
+
+# Unit roundoff and half the subnormal spacing of the 16-bit input types, for
+# weight_rounding_error_bound: fp16 has an 11-bit significand and subnormal
+# spacing 2^-24; bf16 an 8-bit significand and subnormal spacing 2^-133.
+ROUNDING_16 = {"f16": (2.0 ** -11, 2.0 ** -25), "bf16": (2.0 ** -8, 2.0 ** -134)}
+
+
+def weight_rounding_error_bound(q, k, v, scale: float, causal: bool = False, rows=None,
+                                u: float = 2.0 ** -4, a: float = 2.0 ** -10
+                                ) -> Tuple[np.ndarray, np.ndarray]:
     """Bound on |O_hat - O| (per element) and |LSE_hat - LSE| (per row) for a
     forward pass that computes the scores exactly enough and rounds each
-    softmax weight to e4m3 before the P V product and the row sum.
+    softmax weight to a narrower type before the P V product and the row sum
+    (e4m3 for the 8-bit pass, the input type for the 16-bit pass).
 
     Derivation.  The pass weights key j by w_j = 2^(c*s_j - m_ref) for a
-    reference m_ref in [m_max - 8, m_max], rounds it to nearest-even e4m3 and
-    uses the rounded weights in both sums.  Rounding to e4m3 moves a weight by
-    at most half a unit in the last place: relative 2^-4 in the normal range,
-    absolute 2^-10 below 2^-6 (subnormals, spacing 2^-9).  So
+    reference m_ref in [m_max - 8, m_max], rounds it to nearest-even in the
+    narrow type and uses the rounded weights in both sums.  Rounding moves a
+    weight by at most half a unit in the last place: relative u in the normal
+    range, at most an absolute a among the subnormals.  So
     |w_hat_j - w_j| <= e_j = max(u * w_j, a).  With W = sum w_j and
     E = sum e_j,
         O_hat - O = sum_j (w_hat_j - w_j)(v_j - O) / sum_j w_hat_j
@@ -349,6 +368,34 @@ def fp8_weight_error_bound(q, k, v, scale: float, causal: bool = False, rows=Non
                 bO[b, h, r0:r0 + len(idx)] = np.einsum("rj,rjc->rc", e, dev) / (W - E)[:, None]
                 bL[b, h, r0:r0 + len(idx)] = -np.log1p(-E / W)
     return bO, bL
+
+
+def forward_error_bound_16(q, k, v, scale: float, causal: bool, dtype: str, rows=None
+                           ) -> np.ndarray:
+    """Per-element bound on |O_hat - O| for a 16-bit forward pass (``dtype``
+    "f16" or "bf16"), first order in the unit roundoff u of that type.
+
+    Such a pass multiplies 16-bit inputs exactly and accumulates in fp32, so
+    the two roundings it adds on purpose dominate: each softmax weight is
+    rounded to the input type before the P V product and the row sum (bounded
+    by ``weight_rounding_error_bound`` with that type's u and subnormal floor
+    a), and O itself is rounded to the input type when it is stored, which
+    moves an element x by at most half its spacing, u * 2^floor(log2 |x|), or
+    a below the normal range.  The value rounded is within the first term of
+    O, so the spacing is taken at |O| plus that term.  The bound is the sum of
+    the two.  For the unit-variance inputs and 1/sqrt(d) scale of the
+    benchmark workloads it lies below the fixed tolerances; it exceeds them
+    only where large scores make the softmax nearly one-hot and |O| approaches
+    the largest |v| of a row (the second term alone is 2e-3 at |O| = 4 in
+    fp16).
+    """
+    u, a = ROUNDING_16[dtype]
+    bO, _ = weight_rounding_error_bound(q, k, v, scale, causal, rows, u, a)
+    O, _ = attention_forward(q, k, v, scale, causal, rows=rows)
+    x = np.abs(O) + bO
+    with np.errstate(divide="ignore"):
+        half_spacing = u * np.exp2(np.floor(np.log2(x)))
+    return bO + np.maximum(half_spacing, a)
 
 
 def attention_backward(q, k, v, do, scale: float, causal: bool = False):

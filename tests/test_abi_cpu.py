@@ -350,3 +350,43 @@ def test_bwd_workspace_size(L):
     assert L.flash_attn_bwd_workspace_size(2, 3, 100) == 2 * 3 * 100 * 8
     assert L.flash_attn_bwd_workspace_size(0, 3, 100) == 0
     assert L.flash_attn_bwd_workspace_size(1 << 30, 1 << 20, 1 << 20) == -1
+
+
+# ---- backward: workspace contract ---------------------------------------------
+# Fake device addresses for the nine tensors and the workspace, 64 GiB apart.
+DQ, DK, DV, DO_, WS = (0x10000000000 + i * 64 * GiB for i in range(5, 10))
+
+
+def _bwd(L, ws=WS, ws_bytes=None, dq=DQ, B=1, H=2, N=100, d=64, dtype=1):
+    if ws_bytes is None:
+        ws_bytes = L.flash_attn_bwd_workspace_size(B, H, N)
+    st = L.flash_attn_bwd(Q, K, V, O, DO_, LSE, dq, DK, DV, B, H, N, d, 0.125, 0,
+                          ws, ws_bytes, dtype, None)
+    return st, L.flash_attn_last_error().decode()
+
+
+def test_bwd_workspace_one_byte_short_is_rejected(L):
+    """The prep kernel writes D and LSE * log2(e): 8 bytes per row, all required."""
+    need = 1 * 2 * 100 * 8
+    assert L.flash_attn_bwd_workspace_size(1, 2, 100) == need
+    st, msg = _bwd(L, ws_bytes=need - 1)
+    assert st == 11 and str(need) in msg
+    st, _ = _bwd(L, ws_bytes=need // 2)  # the size of D alone
+    assert st == 11
+
+
+def test_bwd_workspace_of_the_full_size_reaches_the_device_check(L):
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _bwd(L)[0] == 8
+
+
+def test_bwd_workspace_second_half_overlapping_dq_is_an_alias(L):
+    """dq starts inside the second half of the workspace (the LSE * log2(e) part)."""
+    need = L.flash_attn_bwd_workspace_size(1, 2, 100)
+    st, msg = _bwd(L, ws=DQ - need + 16)
+    assert st == 7 and "overlap" in msg
+    # Just past the end is fine (the device check is what stops it here).
+    st, _ = _bwd(L, ws=DQ - need)
+    assert st != 7

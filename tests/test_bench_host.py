@@ -87,3 +87,33 @@ def test_cpu_baseline_record():
     rec = bench.cpu_baseline(w, q, k, v, 0.2)
     assert rec["kind"] == "oracle" and rec["unit"] == "TFLOP/s"
     assert rec["value"] > 0 and rec["cores"] >= 1 and w.name in rec["sample"]
+
+
+def test_cpu_baseline_counts_the_threads_it_used():
+    """The record names the threads of the pool (one per core this process may
+    use, at most 16), the cores the host gives it, and the CPU model; the
+    whole small workload fits the budget."""
+    w = W.WORKLOADS["single_head_f32"]
+    q, k, v = W.workload_inputs(w)
+    rec = bench.cpu_baseline(w, q, k, v, 5.0)
+    cores = len(os.sched_getaffinity(0))
+    assert rec["cores"] == min(cores, 16) and rec["host_cores"] == cores
+    assert isinstance(rec["cpu_model"], str)
+    assert rec["sample"].startswith(f"{w.N} of {w.N} query rows")
+
+
+def test_oracle_pool_stops_starting_units_after_the_budget():
+    import time as _t
+    seen = []
+
+    def run(u):
+        seen.append(u)
+        _t.sleep(0.05)
+        return 1.0
+
+    total, n, el, workers = bench.run_oracle_pool(range(10000), run, 0.2)
+    assert n == total == len(seen) and n < 10000
+    assert el < 5.0
+    # at least one unit, even with no budget
+    total, n, _, _ = bench.run_oracle_pool(range(5), run, 0.0)
+    assert n >= 1

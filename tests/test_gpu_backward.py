@@ -91,6 +91,16 @@ def test_backward_workspace_and_dtype_errors():
     lse = torch.zeros(1, 1, 8, dtype=torch.float32, device=DEV)
     with pytest.raises(FlashAttnError, match="FA_ERR_WORKSPACE"):
         flash_attn_bwd(x, x, x, x, lse, x, workspace=torch.empty(16, dtype=torch.uint8, device=DEV))
+    # 8 bytes per row (D and LSE * log2(e)); one byte short, or the size of D
+    # alone, is rejected before any kernel runs.
+    for nbytes in (8 * 8 - 1, 4 * 8):
+        with pytest.raises(FlashAttnError, match="FA_ERR_WORKSPACE"):
+            flash_attn_bwd(x, x, x, x, lse, x,
+                           workspace=torch.empty(nbytes, dtype=torch.uint8, device=DEV))
+    ws = torch.empty(8 * 8, dtype=torch.uint8, device=DEV)
+    dq, dk, dv = flash_attn_bwd(x, x, x, x, lse, x, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.isfinite(dq).all() and torch.isfinite(dk).all() and torch.isfinite(dv).all()
     y = x.float()
     with pytest.raises(FlashAttnError, match="FA_ERR_DTYPE"):
         flash_attn_bwd(y, y, y, y, lse, y)

@@ -1,13 +1,17 @@
 """HIP path vs the fp64 oracle on identical seeded inputs (needs a gfx950 GPU).
 
 Tolerances: max-abs error against fp64 of 2e-3 for fp16, 1e-2 for bf16 and
-1e-5 for fp32 inputs, applied to O and to LSE alike.
+1e-5 for fp32 inputs, applied to O and to LSE alike.  Only the unusual-scale
+test departs from them, with the bound derived for its inputs (see there).
 """
+import time
+
 import numpy as np
 import pytest
 import torch
 
 import oracle
+from oracle_pool import forward_by_heads, host_cores
 from io_aware_tiled_08_amd import FlashAttnError, flash_attn_fwd
 from io_aware_tiled_08_amd import workloads as W
 
@@ -28,9 +32,13 @@ def gpu_forward(q, k, v, scale, causal, stream=None):
     return o, lse
 
 
-def check(o, lse, q, k, v, scale, causal, dtype, rows=None, label="", tol=None):
+def check(o, lse, q, k, v, scale, causal, dtype, rows=None, label="", tol=None, ref=None):
+    """Max-abs error of O and LSE against the oracle.  ``tol`` is a number or,
+    for O, an array of per-element bounds (LSE then takes the fixed one);
+    ``ref`` a precomputed oracle result for these inputs and rows."""
     tol = TOL[dtype] if tol is None else tol
-    O_ref, L_ref = oracle.attention_forward(q, k, v, scale, causal, rows=rows)
+    tol_l = tol if np.isscalar(tol) else TOL[dtype]
+    O_ref, L_ref = oracle.attention_forward(q, k, v, scale, causal, rows=rows) if ref is None else ref
     O = o.double().cpu().numpy()
     L = lse.double().cpu().numpy()
     if rows is not None:
@@ -38,11 +46,13 @@ def check(o, lse, q, k, v, scale, causal, dtype, rows=None, label="", tol=None):
         O = np.take_along_axis(O, idx[..., None], axis=2)
         L = np.take_along_axis(L, idx, axis=2)
     assert np.isfinite(O).all() and np.isfinite(L).all(), f"{label}: non-finite output"
-    err_o = float(np.max(np.abs(O - O_ref))) if O.size else 0.0
+    d_o = np.abs(O - O_ref)
+    err_o = float(np.max(d_o)) if O.size else 0.0
     err_l = float(np.max(np.abs(L - L_ref))) if L.size else 0.0
-    print(f"{label}: max|dO|={err_o:.3e} max|dLSE|={err_l:.3e}", flush=True)
-    assert err_o <= tol, f"{label}: O error {err_o:.3e} > {tol}"
-    assert err_l <= tol, f"{label}: LSE error {err_l:.3e} > {tol}"
+    ratio = float(np.max(d_o / tol)) if O.size else 0.0
+    print(f"{label}: max|dO|={err_o:.3e} max|dLSE|={err_l:.3e} max|dO|/tol={ratio:.3f}", flush=True)
+    assert ratio <= 1.0, f"{label}: O error {err_o:.3e}, {ratio:.3f} of its bound"
+    assert err_l <= tol_l, f"{label}: LSE error {err_l:.3e} > {tol_l}"
     return err_o, err_l
 
 
@@ -72,12 +82,23 @@ def test_batch_and_head_indexing(dtype):
 @pytest.mark.parametrize("dtype", ["f16", "bf16", "f32"])
 def test_unusual_scales(dtype, scale):
     """Scores here reach |scale| * sqrt(d) standard deviations (17 for 1.5 at
-    d=128).  An fp32 dot product carries a rounding error proportional to
-    the score's size, and that error moves O and LSE by the same amount, so
-    the bound grows with max(1, |scale| * sqrt(d))."""
+    d=128), far from the workloads' statistics.
+    fp32: the products and sums of an fp32 dot product round relative to the
+    score's size, and that error moves O and LSE by the same amount, so the
+    bound grows with max(1, |scale| * sqrt(d)).
+    fp16/bf16: the products are exact and the rounding of the scores is
+    negligible; the errors are the rounding of each weight and of O to the
+    input type, both relative.  With nearly one-hot rows O approaches single
+    rows of V and the output rounding alone nears the fixed fp16 tolerance, so
+    each element may use the derived bound of those two roundings
+    (oracle.forward_error_bound_16) where it exceeds the fixed tolerance; LSE
+    keeps the fixed tolerance."""
     q, k, v = W.random_qkv(1, 2, 200, 128, dtype, seed=5)
-    tol = TOL[dtype] * max(1.0, abs(scale) * 128 ** 0.5)
     for causal in (False, True):
+        if dtype == "f32":
+            tol = TOL[dtype] * max(1.0, abs(scale) * 128 ** 0.5)
+        else:
+            tol = np.maximum(TOL[dtype], oracle.forward_error_bound_16(q, k, v, scale, causal, dtype))
         o, lse = gpu_forward(q, k, v, scale, causal)
         check(o, lse, q, k, v, scale, causal, dtype, tol=tol,
               label=f"{dtype} scale={scale} causal={causal}")
@@ -171,17 +192,6 @@ def test_empty_sequence():
 
 # --- the named workloads, in the launch configuration the benchmark times ---
 
-def _boundary_rows(N, count, seed):
-    """Sampled query rows plus the first/last rows and rows around every
-    1024-row boundary."""
-    base = set(range(0, min(N, 4))) | set(range(max(0, N - 4), N))
-    for b in range(0, N, 1024):
-        base |= {x for x in (b - 1, b, b + 1) if 0 <= x < N}
-    rng = np.random.default_rng([seed, 99])
-    rest = rng.choice(N, size=min(N, count), replace=False)
-    return np.array(sorted(base | set(int(x) for x in rest)), dtype=np.int64)
-
-
 def _run_workload(name, rows=None):
     w = W.WORKLOADS[name]
     q, k, v = W.workload_inputs(w)
@@ -191,18 +201,22 @@ def _run_workload(name, rows=None):
     return w, q, k, v, o, lse
 
 
-@pytest.mark.parametrize("name", ["single_head_f32", "batch_f16_d64", "batch_f16_d64_causal"])
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["single_head_f32", "batch_f16_d64", "batch_f16_d64_causal",
+                                  "headline_f16_d128", "rescale_stress_bf16"])
 def test_workload_full(name):
+    """Every row of every head against the oracle, at the fixed tolerances.
+    The oracle runs head by head on the host's cores (tests/oracle_pool.py)."""
     w, q, k, v, o, lse = _run_workload(name)
-    check(o, lse, q, k, v, w.scale, w.causal, w.dtype, label=name)
+    t0 = time.time()
 
+    def progress(done, total):
+        if done == total or done % max(1, total // 4) == 0:
+            print(f"  oracle: {done}/{total} heads, {time.time() - t0:.1f} s", flush=True)
 
-@pytest.mark.parametrize("name", ["headline_f16_d128", "rescale_stress_bf16"])
-def test_workload_sampled(name):
-    w, q, k, v, o, lse = _run_workload(name)
-    rows = _boundary_rows(w.N, 256, w.seed)
-    check(o, lse, q, k, v, w.scale, w.causal, w.dtype, rows=rows, label=name)
-    assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+    ref = forward_by_heads(q, k, v, w.scale, w.causal, progress=progress)
+    print(f"  oracle on {host_cores()} cores: {time.time() - t0:.1f} s", flush=True)
+    check(o, lse, q, k, v, w.scale, w.causal, w.dtype, label=name, ref=ref)
 
 
 def test_workload_long_context():
