@@ -28,7 +28,7 @@
 extern "C" {
 #endif
 
-#define FA_MI355X_ABI_VERSION 6
+#define FA_MI355X_ABI_VERSION 7
 
 typedef enum {
   FA_F32 = 0,   /* IEEE binary32 */
@@ -189,6 +189,41 @@ fa_status flash_attn_fwd_kvcache(const void* q, const void* k, const void* v,
                                  int num_splits, void* workspace,
                                  int64_t workspace_bytes,
                                  fa_dtype dtype, void* stream);
+
+/* Bytes of device scratch the library holds on each GPU it runs on, for
+ * flash_attn_fwd_kvcache_noalloc (held from its first call on that GPU
+ * until the process ends). */
+#define FA_MI355X_KVCACHE_SCRATCH_BYTES (16 * 1024 * 1024)
+
+/*
+ * flash_attn_fwd_kvcache_noalloc -- flash_attn_fwd_kvcache without a
+ * workspace argument and without any allocation.
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * computation, arguments (less workspace and workspace_bytes), kernels,
+ * key-split choice and results as flash_attn_fwd_kvcache: bit for bit equal
+ * for the same num_splits.  The split partials go to a static device array of
+ * the library (FA_MI355X_KVCACHE_SCRATCH_BYTES per GPU) instead of a caller's
+ * workspace; its address on the current device is looked up once
+ * (hipGetSymbolAddress) on the first call that needs it.  The call never
+ * calls hipMalloc, hipFree or any allocating routine.
+ *
+ * Returns FA_ERR_WORKSPACE, before any HIP call, when the chosen splits need
+ * more than FA_MI355X_KVCACHE_SCRATCH_BYTES
+ * (flash_attn_kvcache_workspace_size() tells the size; pass fewer num_splits
+ * or use flash_attn_fwd_kvcache).  Every call on one GPU shares that GPU's
+ * array: calls that may overlap in time on one GPU (different streams, or
+ * different host threads) race and give wrong results; order them on one
+ * stream.  The stream must belong to the current device.  Other errors as for
+ * flash_attn_fwd_kvcache.
+ */
+fa_status flash_attn_fwd_kvcache_noalloc(const void* q, const void* k,
+                                         const void* v, void* o, float* lse,
+                                         int64_t B, int64_t H, int64_t Nq,
+                                         int64_t Nk, int64_t d, float scale,
+                                         int causal, int num_splits,
+                                         fa_dtype dtype, void* stream);
 
 /*
  * flash_attn_fwd_fp8 -- the forward pass of flash_attn_fwd on 8-bit inputs.

@@ -23,10 +23,10 @@ STATUS = {
     8: "FA_ERR_NO_DEVICE", 9: "FA_ERR_ARCH", 10: "FA_ERR_HIP", 11: "FA_ERR_WORKSPACE",
 }
 STATUS_CODE = {name: code for code, name in STATUS.items()}
-EXPORTS = ("flash_attn_fwd", "flash_attn_fwd_persistent", "flash_attn_bwd", "flash_attn_bwd_workspace_size", "flash_attn_fwd_fp8", "flash_attn_fwd_kvcache", "flash_attn_kvcache_splits",
-           "flash_attn_kvcache_workspace_size", "flash_attn_status_str",
+EXPORTS = ("flash_attn_fwd", "flash_attn_fwd_persistent", "flash_attn_bwd", "flash_attn_bwd_workspace_size", "flash_attn_fwd_fp8", "flash_attn_fwd_kvcache", "flash_attn_fwd_kvcache_noalloc",
+           "flash_attn_kvcache_splits", "flash_attn_kvcache_workspace_size", "flash_attn_status_str",
            "flash_attn_last_error", "flash_attn_abi_version")
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 _lib = None
 _lock = threading.Lock()
@@ -74,6 +74,10 @@ def lib() -> ctypes.CDLL:
                 ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64,
                 ctypes.c_int, ctypes.c_void_p]
             L.flash_attn_fwd_kvcache.restype = ctypes.c_int
+            L.flash_attn_fwd_kvcache_noalloc.argtypes = [ctypes.c_void_p] * 5 + [
+                ctypes.c_int64] * 5 + [ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_void_p]
+            L.flash_attn_fwd_kvcache_noalloc.restype = ctypes.c_int
             L.flash_attn_kvcache_splits.argtypes = [ctypes.c_int64] * 5 + [ctypes.c_int]
             L.flash_attn_kvcache_splits.restype = ctypes.c_int
             L.flash_attn_kvcache_workspace_size.argtypes = [ctypes.c_int64] * 5 + [ctypes.c_int]
@@ -213,19 +217,9 @@ def flash_attn_fwd_kvcache_ptr(q: int, k: int, v: int, o: int, lse: int, B: int,
                                         workspace_bytes, dtype, stream)
 
 
-def flash_attn_fwd_kvcache(q, k, v, o=None, lse=None, *, scale: Optional[float] = None,
-                           causal: bool = False, num_splits: int = 0, workspace=None,
-                           stream=None) -> Tuple["object", "object"]:
-    """Attention of q [B, H, Nq, d] against a key/value cache k, v [B, H, Nk, d].
-
-    float16 or bfloat16 device tensors, contiguous.  causal: the queries are
-    the last Nq of Nk positions, query i sees keys j <= i + Nk - Nq.
-    num_splits <= 0 lets the library choose how many key ranges to compute
-    separately and merge.  workspace: optional device tensor of at least
-    kvcache_workspace_size(...) bytes; allocated here when needed and omitted.
-    o, lse: optional preallocated outputs.  Enqueued on `stream` (default: the
-    current stream of q's device) without synchronising.
-    """
+def _check_kvcache_tensors(q, k, v, o, lse):
+    """Shapes, dtypes, devices and contiguity of a cache call's tensors;
+    returns (B, H, Nq, Nk, d, dtype code)."""
     import torch
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
@@ -241,17 +235,61 @@ def flash_attn_fwd_kvcache(q, k, v, o=None, lse=None, *, scale: Optional[float] 
     if k.device != q.device or v.device != q.device:
         raise ValueError("q, k and v must be on the same device")
     code = _dtype_code(q)
+    if (not isinstance(o, torch.Tensor) or o.shape != q.shape or o.dtype != q.dtype
+            or o.device != q.device or not o.is_contiguous()):
+        raise ValueError("o must be a contiguous tensor like q")
+    if (not isinstance(lse, torch.Tensor) or lse.shape != (B, H, Nq)
+            or lse.dtype != torch.float32 or lse.device != q.device or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor on q's device")
+    return B, H, Nq, Nk, d, code
+
+
+def flash_attn_fwd_kvcache_noalloc(q, k, v, o, lse, *, scale: Optional[float] = None,
+                                   causal: bool = False, num_splits: int = 0, stream=None):
+    """flash_attn_fwd_kvcache with the split partials in the library's own
+    static device scratch (FA_MI355X_KVCACHE_SCRATCH_BYTES per GPU): neither
+    the library nor this function allocates anything, so o and lse must be
+    passed.  Calls that may overlap in time on one GPU race on that scratch;
+    order them on one stream.  Enqueued on `stream` (default: the current
+    stream of q's device) without synchronising; returns (o, lse)."""
+    import torch
+    B, H, Nq, Nk, d, code = _check_kvcache_tensors(q, k, v, o, lse)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    L = lib()
+    with torch.cuda.device(q.device):
+        s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        st = L.flash_attn_fwd_kvcache_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                              o.data_ptr(), lse.data_ptr(), B, H, Nq, Nk, d,
+                                              float(scale), int(bool(causal)), int(num_splits),
+                                              code, s.cuda_stream)
+    if st != 0:
+        raise FlashAttnError(st, L.flash_attn_last_error().decode())
+    return o, lse
+
+
+def flash_attn_fwd_kvcache(q, k, v, o=None, lse=None, *, scale: Optional[float] = None,
+                           causal: bool = False, num_splits: int = 0, workspace=None,
+                           stream=None) -> Tuple["object", "object"]:
+    """Attention of q [B, H, Nq, d] against a key/value cache k, v [B, H, Nk, d].
+
+    float16 or bfloat16 device tensors, contiguous.  causal: the queries are
+    the last Nq of Nk positions, query i sees keys j <= i + Nk - Nq.
+    num_splits <= 0 lets the library choose how many key ranges to compute
+    separately and merge.  workspace: optional device tensor of at least
+    kvcache_workspace_size(...) bytes; allocated here when needed and omitted.
+    o, lse: optional preallocated outputs.  Enqueued on `stream` (default: the
+    current stream of q's device) without synchronising.
+    """
+    import torch
     if o is None:
         o = torch.empty_like(q)
     if lse is None:
-        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    if o.shape != q.shape or o.dtype != q.dtype or o.device != q.device or not o.is_contiguous():
-        raise ValueError("o must be a contiguous tensor like q")
-    if (lse.shape != (B, H, Nq) or lse.dtype != torch.float32 or lse.device != q.device
-            or not lse.is_contiguous()):
-        raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor on q's device")
+        lse = torch.empty((q.shape[0], q.shape[1], q.shape[2]), dtype=torch.float32,
+                          device=q.device)
+    B, H, Nq, Nk, d, code = _check_kvcache_tensors(q, k, v, o, lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
     L = lib()
     need = L.flash_attn_kvcache_workspace_size(B, H, Nq, Nk, d, int(num_splits))
     if need < 0:

@@ -373,12 +373,17 @@ int64_t flash_attn_kvcache_workspace_size(int64_t B, int64_t H, int64_t Nq, int6
   return kv_workspace_bytes(B * H, Nq, d, S);
 }
 
-fa_status flash_attn_fwd_kvcache(const void* q, const void* k, const void* v, void* o,
-                                 float* lse, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
-                                 int64_t d, float scale, int causal, int num_splits,
-                                 void* workspace, int64_t workspace_bytes, fa_dtype dtype,
-                                 void* stream) {
-  g_last_error[0] = '\0';
+namespace {
+
+// Argument checks shared by the two cache entry points, in the order both
+// document (everything before any HIP call).  FA_OK with *empty true for an
+// empty problem; otherwise *a is filled except for the workspace, and *need
+// is the scratch the chosen key splits take (0 for one split).
+fa_status check_kvcache(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int64_t B, int64_t H, int64_t Nq, int64_t Nk, int64_t d, float scale,
+                        int causal, int num_splits, fa_dtype dtype, fa::KvArgs* a,
+                        int64_t* need, bool* empty) {
+  *empty = false;
   if (B < 0 || H < 0 || Nq < 0 || Nk < 0)
     return fail(FA_ERR_SHAPE, "B, H, Nq, Nk must be >= 0 (got %lld, %lld, %lld, %lld)",
                 (long long)B, (long long)H, (long long)Nq, (long long)Nk);
@@ -386,7 +391,10 @@ fa_status flash_attn_fwd_kvcache(const void* q, const void* k, const void* v, vo
   if (dtype != FA_F16 && dtype != FA_BF16)
     return fail(FA_ERR_DTYPE, "the key/value-cache path takes FA_F16 or FA_BF16 (got %d)", (int)dtype);
   if (!std::isfinite(scale)) return fail(FA_ERR_SCALE, "scale must be finite");
-  if (B == 0 || H == 0 || Nq == 0) return FA_OK;
+  if (B == 0 || H == 0 || Nq == 0) {
+    *empty = true;
+    return FA_OK;
+  }
   if (Nk == 0) return fail(FA_ERR_SHAPE, "Nk = 0: the queries see no key");
   if (causal && Nk < Nq)
     return fail(FA_ERR_SHAPE, "causal queries are the last Nq of Nk positions: need Nk >= Nq "
@@ -408,16 +416,7 @@ fa_status flash_attn_fwd_kvcache(const void* q, const void* k, const void* v, vo
       (sp.n_split > 1 && BH * Nq > (int64_t)UINT32_MAX / 256))
     return fail(FA_ERR_SHAPE, "B*H*ceil(Nq/%d)*splits = %lld workgroups exceeds the grid limit",
                 fa::kKvRows, (long long)(BH * nqb * sp.n_split));
-  const int64_t need = kv_workspace_bytes(BH, Nq, d, sp.n_split);
-  if (need > 0) {
-    if (!workspace)
-      return fail(FA_ERR_WORKSPACE, "%d key splits need a workspace of %lld bytes", sp.n_split,
-                  (long long)need);
-    if ((uintptr_t)workspace & 15u) return fail(FA_ERR_ALIGN, "workspace must be 16-byte aligned");
-    if (workspace_bytes < need)
-      return fail(FA_ERR_WORKSPACE, "workspace has %lld bytes, %d key splits need %lld",
-                  (long long)workspace_bytes, sp.n_split, (long long)need);
-  }
+  *need = kv_workspace_bytes(BH, Nq, d, sp.n_split);
 
   const int64_t qbytes = BH * Nq * d * elem;
   const int64_t kbytes = BH * Nk * d * elem;
@@ -427,34 +426,90 @@ fa_status flash_attn_fwd_kvcache(const void* q, const void* k, const void* v, vo
       overlaps(lse, lbytes, k, kbytes) || overlaps(lse, lbytes, v, kbytes) ||
       overlaps(lse, lbytes, o, qbytes))
     return fail(FA_ERR_ALIAS, "o and lse must not overlap q, k, v or each other");
-  if (need > 0 && (overlaps(workspace, need, q, qbytes) || overlaps(workspace, need, k, kbytes) ||
-                   overlaps(workspace, need, v, kbytes) || overlaps(workspace, need, o, qbytes) ||
-                   overlaps(workspace, need, lse, lbytes)))
-    return fail(FA_ERR_ALIAS, "the workspace must not overlap q, k, v, o or lse");
 
-  fa_status st = check_device();
-  if (st != FA_OK) return st;
+  a->q = q;
+  a->k = k;
+  a->v = v;
+  a->o = o;
+  a->lse = lse;
+  a->workspace = nullptr;
+  a->BH = BH;
+  a->Nq = Nq;
+  a->Nk = Nk;
+  a->d = (int)d;
+  a->scale = scale;
+  a->causal = causal != 0;
+  a->dtype = (fa::Dtype)dtype;
+  a->n_split = sp.n_split;
+  a->tiles_per_split = sp.tiles_per_split;
+  return FA_OK;
+}
 
-  fa::KvArgs a;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.o = o;
-  a.lse = lse;
-  a.workspace = need > 0 ? workspace : nullptr;
-  a.BH = BH;
-  a.Nq = Nq;
-  a.Nk = Nk;
-  a.d = (int)d;
-  a.scale = scale;
-  a.causal = causal != 0;
-  a.dtype = (fa::Dtype)dtype;
-  a.n_split = sp.n_split;
-  a.tiles_per_split = sp.tiles_per_split;
+fa_status launch_kvcache_checked(const fa::KvArgs& a, void* stream) {
   (void)hipGetLastError();
   const hipError_t e = fa::launch_kvcache(a, (hipStream_t)stream);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return FA_OK;
+}
+
+}  // namespace
+
+fa_status flash_attn_fwd_kvcache(const void* q, const void* k, const void* v, void* o,
+                                 float* lse, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                                 int64_t d, float scale, int causal, int num_splits,
+                                 void* workspace, int64_t workspace_bytes, fa_dtype dtype,
+                                 void* stream) {
+  g_last_error[0] = '\0';
+  fa::KvArgs a;
+  int64_t need = 0;
+  bool empty = false;
+  fa_status st = check_kvcache(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, num_splits,
+                               dtype, &a, &need, &empty);
+  if (st != FA_OK || empty) return st;
+  if (need > 0) {
+    if (!workspace)
+      return fail(FA_ERR_WORKSPACE, "%d key splits need a workspace of %lld bytes", a.n_split,
+                  (long long)need);
+    if ((uintptr_t)workspace & 15u) return fail(FA_ERR_ALIGN, "workspace must be 16-byte aligned");
+    if (workspace_bytes < need)
+      return fail(FA_ERR_WORKSPACE, "workspace has %lld bytes, %d key splits need %lld",
+                  (long long)workspace_bytes, a.n_split, (long long)need);
+    const int64_t qbytes = a.BH * Nq * d * 2, kbytes = a.BH * Nk * d * 2, lbytes = a.BH * Nq * 4;
+    if (overlaps(workspace, need, q, qbytes) || overlaps(workspace, need, k, kbytes) ||
+        overlaps(workspace, need, v, kbytes) || overlaps(workspace, need, o, qbytes) ||
+        overlaps(workspace, need, lse, lbytes))
+      return fail(FA_ERR_ALIAS, "the workspace must not overlap q, k, v, o or lse");
+    a.workspace = workspace;
+  }
+  st = check_device();
+  if (st != FA_OK) return st;
+  return launch_kvcache_checked(a, stream);
+}
+
+fa_status flash_attn_fwd_kvcache_noalloc(const void* q, const void* k, const void* v, void* o,
+                                         float* lse, int64_t B, int64_t H, int64_t Nq, int64_t Nk,
+                                         int64_t d, float scale, int causal, int num_splits,
+                                         fa_dtype dtype, void* stream) {
+  g_last_error[0] = '\0';
+  fa::KvArgs a;
+  int64_t need = 0;
+  bool empty = false;
+  fa_status st = check_kvcache(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, num_splits,
+                               dtype, &a, &need, &empty);
+  if (st != FA_OK || empty) return st;
+  if (need > fa::kKvScratchBytes)
+    return fail(FA_ERR_WORKSPACE,
+                "%d key splits need %lld bytes of scratch; the library's scratch holds %lld "
+                "(fewer splits, or flash_attn_fwd_kvcache with a workspace)",
+                a.n_split, (long long)need, (long long)fa::kKvScratchBytes);
+  st = check_device();
+  if (st != FA_OK) return st;
+  if (need > 0) {
+    const hipError_t e = fa::kvcache_scratch(&a.workspace);
+    if (e != hipSuccess)
+      return fail(FA_ERR_HIP, "scratch address lookup failed: %s", hipGetErrorString(e));
+  }
+  return launch_kvcache_checked(a, stream);
 }
 
 const char* flash_attn_status_str(fa_status s) {

@@ -29,6 +29,8 @@
 //     across waves.  A workgroup writes the final O and LSE when there is one
 //     split, otherwise its range's normalised O and its LSE to the workspace,
 //     and the merge kernel below combines the ranges with the same rule.
+#include <mutex>
+
 #include "fa_device.h"
 #include "fa_f16_common.h"
 #include "fa_kvcache.h"
@@ -432,6 +434,35 @@ hipError_t launch_t(const KvArgs& a, hipStream_t s) {
 
 hipError_t launch_kvcache(const KvArgs& a, hipStream_t stream) {
   return a.dtype == Dtype::BF16 ? launch_t<__bf16>(a, stream) : launch_t<_Float16>(a, stream);
+}
+
+// Split partials of the allocation-free entry point.  Each GPU holds its own
+// copy of this array at its own address; host code never uses the name as an
+// address (it is a host-side stand-in), only the pointer that
+// hipGetSymbolAddress returns for the current device.  Every entry is written
+// by the split kernel before the merge kernel reads it, so nothing needs
+// clearing between calls; calls that overlap on one GPU share the array and
+// race.
+static __device__ __align__(256) char scratch[kKvScratchBytes];
+
+hipError_t kvcache_scratch(void** ptr) {
+  constexpr int kMaxDev = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDev] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!a) return hipErrorInvalidSymbol;
+    addr[dev] = a;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace fa

@@ -353,11 +353,11 @@ def test_bwd_workspace_size(L):
 
 
 # ---- backward: workspace contract ---------------------------------------------
-# Fake device addresses for the nine tensors and the workspace, 64 GiB apart.
-DQ, DK, DV, DO_, WS = (0x10000000000 + i * 64 * GiB for i in range(5, 10))
+# Fake device addresses for the gradients, dO and the workspace, 64 GiB apart.
+DQ, DK, DV, DO_, BWS = (0x10000000000 + i * 64 * GiB for i in range(6, 11))
 
 
-def _bwd(L, ws=WS, ws_bytes=None, dq=DQ, B=1, H=2, N=100, d=64, dtype=1):
+def _bwd(L, ws=BWS, ws_bytes=None, dq=DQ, B=1, H=2, N=100, d=64, dtype=1):
     if ws_bytes is None:
         ws_bytes = L.flash_attn_bwd_workspace_size(B, H, N)
     st = L.flash_attn_bwd(Q, K, V, O, DO_, LSE, dq, DK, DV, B, H, N, d, 0.125, 0,
@@ -390,3 +390,47 @@ def test_bwd_workspace_second_half_overlapping_dq_is_an_alias(L):
     # Just past the end is fine (the device check is what stops it here).
     st, _ = _bwd(L, ws=DQ - need)
     assert st != 7
+
+
+# ---- flash_attn_fwd_kvcache_noalloc: the same checks, the scratch limit -----
+
+def _kvn(L, q=Q, k=K, v=V, o=O, lse=LSE, B=2, H=3, Nq=4, Nk=1000, d=64, scale=0.125,
+         causal=0, splits=0, dtype=1):
+    st = L.flash_attn_fwd_kvcache_noalloc(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal,
+                                          splits, dtype, None)
+    return st, L.flash_attn_last_error().decode()
+
+
+def test_noalloc_scratch_size_matches_the_header(L):
+    m = re.search(r"#define\s+FA_MI355X_KVCACHE_SCRATCH_BYTES\s+\((\d+) \* (\d+) \* (\d+)\)",
+                  _header())
+    assert m and int(m.group(1)) * int(m.group(2)) * int(m.group(3)) == 16 << 20
+
+
+def test_noalloc_argument_checks_match_the_workspace_entry_point(L):
+    """Every argument error of flash_attn_fwd_kvcache (other than the
+    workspace's own) comes back with the same code, before any HIP call."""
+    for kw in ({"q": None}, {"lse": None}, {"B": -1}, {"Nk": -1}, {"d": 96}, {"dtype": 0},
+               {"dtype": 7}, {"v": V + 8}, {"scale": math.nan}, {"o": K}, {"lse": K + 64},
+               {"Nk": 0}, {"Nq": 10, "Nk": 9, "causal": 1}):
+        assert _kvn(L, **kw)[0] == _kv(L, **kw)[0] != 0, kw
+    assert _kvn(L, B=0, q=None, o=None, lse=None) == (0, "")
+
+
+def test_noalloc_rejects_splits_beyond_the_scratch(L):
+    """Two splits of one head at d=64 take 2 * Nq * 65 * 4 bytes: 32263 query
+    rows fit 16 MiB, 32264 do not."""
+    cap = 16 << 20
+    assert L.flash_attn_kvcache_workspace_size(1, 1, 32263, 32768, 64, 2) <= cap
+    assert L.flash_attn_kvcache_workspace_size(1, 1, 32264, 32768, 64, 2) > cap
+    st, msg = _kvn(L, B=1, H=1, Nq=32264, Nk=32768, splits=2)
+    assert st == 11 and "scratch" in msg and str(cap) in msg
+
+
+def test_noalloc_no_device_reported_not_crashed(L):
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _kvn(L, B=1, H=1, Nq=32263, Nk=32768, splits=2)[0] == 8
+    assert _kvn(L, splits=1)[0] == 8
+    assert _kvn(L)[0] == 8
