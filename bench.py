@@ -288,8 +288,21 @@ class ClockSampler:
     def __init__(self, period_s=0.01):
         self.period_s = period_s
         self.samples = []
+        self.power = []
         self._stop = None
         self._thread = None
+
+    def _power(self, amdsmi, h):
+        """Socket power in watts, or None."""
+        try:
+            info = amdsmi.amdsmi_get_power_info(h)
+        except Exception:
+            return None
+        for key in ("current_socket_power", "socket_power", "average_socket_power"):
+            x = info.get(key) if isinstance(info, dict) else None
+            if isinstance(x, (int, float)) and 0 < x < 5000:
+                return float(x)
+        return None
 
     def _read(self, amdsmi, h):
         try:
@@ -329,6 +342,9 @@ class ClockSampler:
                     return
                 if x:
                     self.samples.append((time.perf_counter(), x))
+                w = self._power(amdsmi, h)
+                if w:
+                    self.power.append((time.perf_counter(), w))
                 self._stop.wait(self.period_s)
 
         self._thread = threading.Thread(target=run, daemon=True)
@@ -344,9 +360,9 @@ class ClockSampler:
         except Exception:
             pass
 
-    def window(self, t0, t1):
-        """Samples taken between perf_counter times t0 and t1."""
-        return [x for t, x in self.samples if t0 <= t <= t1]
+    def window(self, t0, t1, power=False):
+        """Clock (or power) samples taken between perf_counter times t0 and t1."""
+        return [x for t, x in (self.power if power else self.samples) if t0 <= t <= t1]
 
 
 def cpu_baseline_cache(w, q, k, v, budget_s: float):
@@ -543,6 +559,8 @@ def main():
     per_launch = sorted(a.elapsed_time(b) for a, b in pairs)
     clk = sorted(clock.window(t_d, t_d_end))
     mhz = clk[len(clk) // 2] if len(clk) >= MIN_CLOCK_SAMPLES else None
+    pw = sorted(clock.window(t_d, t_d_end, power=True))
+    watts = pw[len(pw) // 2] if len(pw) >= MIN_CLOCK_SAMPLES else None
 
     if args.copy_calibration:
         src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -620,6 +638,8 @@ def main():
             # left out.
             roofline["gfx_clock_mhz_median"] = round(mhz, 1)
             roofline["clock_samples"] = len(clk)
+            if watts:
+                roofline["socket_power_w_median"] = round(watts, 1)
             f = flops / (dist[1] * 1e-3) / 1e12 / (peak * mhz / PEAK_CLOCK_MHZ)
             if 0 < f <= 1:
                 roofline["frac_at_measured_clock"] = round(f, 4)

@@ -21,17 +21,22 @@
 //     tile (M phase) the other runs its softmax on the vector ALU (V phase),
 //     and a workgroup barrier swaps the roles.  For tile t a wave's M phase is
 //     O += P(t-1) V(t-1) followed by S(t) = K(t) Q^T, and its V phase turns
-//     S(t) into P(t).  (On gfx950 a 32x32x16 MFMA blocks its SIMD's vector
-//     issue for most of its 32 cycles, so ordinary vector work barely hides
-//     under matrix work; the alternation gives each phase whole slots.)  The
+//     S(t) into P(t).  The softmax's vector instructions issue while the
+//     partner wave's matrix products run (a wave64 fp32 VALU op occupies the
+//     vector pipe 4 cycles, exp 8; a 32x32x16 MFMA the matrix pipe 32).  The
 //     wave in its M phase runs at issue priority 1, its partner at 0.
 //   * K and V tiles (128 keys) are double buffered in LDS and filled by
-//     buffer_load ... lds (HBM/L2 straight into LDS, no register staging),
-//     issued by the group entering its V phase.  Each row's 16-byte chunks
-//     are stored XOR-permuted so that the operand reads hit all LDS banks;
-//     the permutation is applied on the global side (lane i of a load always
-//     writes LDS bytes 16i..16i+15).  Loads for a tile are issued one tile
-//     ahead and only waited for at the barrier before their first use.
+//     buffer_load ... lds (HBM/L2 straight into LDS, no register staging).
+//     The CU's load path takes one 1 KiB piece per about 16 cycles and a wave
+//     issues in order, so a wave that issues a tile's pieces is held until
+//     they are accepted; the two tensors' loads are therefore split between
+//     the groups, each at the start of its own V phase: group B issues K two
+//     tiles ahead, group A issues V for the tile it is turning into P (that
+//     buffer's last reader finished two slots earlier) and waits for it
+//     before the barrier that ends the slot.  Each row's 16-byte chunks are
+//     stored XOR-permuted so that the operand reads hit all LDS banks; the
+//     permutation is applied on the global side (lane i of a load always
+//     writes LDS bytes 16i..16i+15).
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_{f16,bf16}: a lane owns one query
 //     (accumulator column) and 16 keys of each 32-key block, the other 16 sit
 //     in lane l^32, so the row max is in-lane plus one v_permlane32_swap,
@@ -165,8 +170,8 @@ __device__ __forceinline__ void fwd_f16_tiles(const KernelParams& p, const WorkI
   };
 
   // ---- tile loads: global -> LDS, 16 bytes per lane -------------------------
-  // Group B (four waves) loads every tile.  Load j of group-wave gw
-  // covers rows (gw*LPW + j)*RPL .. +RPL of the tile; lane i fills LDS chunk
+  // The four waves of a group share a tile's load (group B the K tiles,
+  // group A the V tiles).  Load j of group-wave gw covers rows (gw*LPW + j)*RPL .. +RPL of the tile; lane i fills LDS chunk
   // slot i%CPR of row .. + i/CPR, which holds global chunk slot ^ mask(row).
   int kvoff[LPW], vvoff[LPW];
 #pragma unroll
@@ -484,11 +489,13 @@ __device__ __forceinline__ void fwd_f16_tiles(const KernelParams& p, const WorkI
   // Global slots: in slot 2t group A runs M(t) and group B runs V(t-1); in
   // slot 2t+1 group A runs V(t) and group B runs M(t).  Both groups execute
   // the same sequence M(0) V(0) M(1) V(1) ... M(n_tiles) V(n_tiles), group B
-  // one slot later (it idles through slot 0).  Group B loads the tiles, at the
-  // start of its V phases: at the start of slot 2t+2 it issues K(t+2) and
-  // V(t+1), which overwrite K(t) and V(t-1) (last read in slot 2t+1) and are
-  // first read in slot 2t+4; it waits for them at the end of its next M phase
-  // (slot 2t+3), before the barrier that closes that slot.  A wave works on
+  // one slot later (it idles through slot 0).  Loads, at the start of V
+  // phases: group B issues K(t+2) at the start of slot 2t+2; it overwrites
+  // K(t) (last read in slot 2t+1), is first read in slot 2t+4, and B waits
+  // for it at the end of its next M phase (slot 2t+3).  Group A issues V(t)
+  // at the start of slot 2t+1; it overwrites V(t-2) (last read in slot 2t-1),
+  // is first read in slot 2t+2, and A waits for it at the end of that same V
+  // phase, before the barrier that closes slot 2t+1.  A wave works on
   // tiles t < wave_tiles only (causal waves above the diagonal stop early)
   // but takes part in every slot's barrier.  The stream runs the same slots,
   // counted in stream steps instead of tiles.
@@ -503,16 +510,16 @@ __device__ __forceinline__ void fwd_f16_tiles(const KernelParams& p, const WorkI
     wave_priority<0>();
     if (group_b) wait_loads();
     barrier();
-    if (group_b) {
+    if (group_b)
       issue_k(t + 2);
-      issue_v(t + 1);
-    }
+    else
+      issue_v(t);
     vwork();
+    if (!group_b) wait_loads();
     barrier();
   };
   if (group_b) {
     issue_k(1);
-    issue_v(0);
     barrier();
   }
   if constexpr (STREAM) {
