@@ -11,9 +11,9 @@ peak, and the fp64 CPU oracle timed on a bounded sample of the same workload.
 Counter workflow (HBM traffic per launch, rocprofv3 on the GPU host):
 
     rocprofv3 --pmc FETCH_SIZE -f csv -d OUT/fetch -o fetch -- \\
-        python3 bench.py --steps 5 --warmup 1 --cpu-budget 0 --copy-calibration
+        python3 bench.py --steps 5 --warmup 1 --settle 0 --dist 0 --cpu-budget 0 --copy-calibration
     rocprofv3 --pmc WRITE_SIZE -f csv -d OUT/write -o write -- \\
-        python3 bench.py --steps 5 --warmup 1 --cpu-budget 0 --copy-calibration
+        python3 bench.py --steps 5 --warmup 1 --settle 0 --dist 0 --cpu-budget 0 --copy-calibration
     python3 bench.py --summarize-traffic OUT/fetch/fetch_counter_collection.csv \\
         OUT/write/write_counter_collection.csv
 
@@ -241,9 +241,11 @@ def summarize_traffic(fetch_csv: str, write_csv: str, workload: str) -> str:
         "Commands (GPU host, from the repository root):",
         "",
         "    rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/traffic_" + workload + "/fetch -o fetch -- \\",
-        f"        python3 bench.py --workload {workload} --steps 5 --warmup 1 --cpu-budget 0 --copy-calibration",
+        f"        python3 bench.py --workload {workload} --steps 5 --warmup 1 --settle 0 --dist 0 "
+        "--cpu-budget 0 --copy-calibration",
         "    rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/traffic_" + workload + "/write -o write -- \\",
-        f"        python3 bench.py --workload {workload} --steps 5 --warmup 1 --cpu-budget 0 --copy-calibration",
+        f"        python3 bench.py --workload {workload} --steps 5 --warmup 1 --settle 0 --dist 0 "
+        "--cpu-budget 0 --copy-calibration",
         "    python3 bench.py --workload " + workload + " --summarize-traffic \\",
         "        gpurun_out/traffic_" + workload + "/fetch/fetch_counter_collection.csv \\",
         "        gpurun_out/traffic_" + workload + "/write/write_counter_collection.csv",
@@ -268,6 +270,81 @@ def summarize_traffic(fetch_csv: str, write_csv: str, workload: str) -> str:
         "",
     ]
     path = traffic_path(workload)
+    with open(path, "w") as f:
+        f.write("\n".join(lines))
+    return path
+
+
+def summarize_trace(trace_dir: str, bench_log: str, workload: str) -> str:
+    """Turns one `rocprofv3 --kernel-trace --stats -f csv` run of bench.py
+    (its output directory and the run's stdout) into
+    profiles/kernel_trace_<workload>.md: the stats table and, per kernel, the
+    average duration of the dispatches that fell in the timed region (the
+    calls after the clock settling and the warm-up steps, as the JSON line
+    reports them), next to the same run's event timing."""
+    w, key = workload_by_name(workload)
+    main_pat, all_pat = KERNEL_NAME_PATTERN[key]
+
+    def find(suffix):
+        for dirpath, _, files in os.walk(trace_dir):
+            for f in files:
+                if f.endswith(suffix):
+                    return os.path.join(dirpath, f)
+        raise SystemExit(f"{trace_dir}: no *{suffix}")
+
+    stats = [r for r in csv.DictReader(open(find("kernel_stats.csv"))) if all_pat in r["Name"]]
+    trace = [r for r in csv.DictReader(open(find("kernel_trace.csv"))) if all_pat in r["Kernel_Name"]]
+    r = json.loads([line for line in open(bench_log) if line.startswith("{")][-1])
+    rf = r["roofline"]
+    first = r.get("clock_settle", {}).get("calls", 0) + r["warmup"]
+    by = {}
+    for t in trace:
+        by.setdefault(t["Kernel_Name"], []).append(
+            (int(t["Start_Timestamp"]), int(t["End_Timestamp"]) - int(t["Start_Timestamp"])))
+    parts, total = [], 0.0
+    for name, v in by.items():
+        v.sort()
+        timed = [d for _, d in v[first:first + r["steps"]]]
+        avg = sum(timed) / len(timed)
+        total += avg
+        parts.append(f"`{name[:70]}` {avg:.0f} ns over {len(timed)} dispatches")
+    ev_ns = rf["kernel_ms"] * 1e6
+    cmd = " ".join(a for a in ["python3 bench.py --workload", workload, "--steps", str(r["steps"]),
+                               "--cpu-budget 0"])
+    lines = [
+        f"# Kernel trace, workload {workload}",
+        "",
+        f"Workload: {w.description}.",
+        "",
+        "Command (GPU host, repository root; then `bench.py --summarize-trace`):",
+        "",
+        f"    rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/prof/trace_{workload} -o trace -- \\",
+        f"        {cmd} > gpurun_out/prof/bench_{workload}.log",
+        f"    python3 bench.py --workload {workload} --summarize-trace gpurun_out/prof/trace_{workload} "
+        f"gpurun_out/prof/bench_{workload}.log",
+        "",
+        "Stats over every dispatch of the run (clock settling, warm-up, timed and per-call timed calls; ns):",
+        "",
+        "| kernel | calls | average ns | min ns | max ns | stddev ns |",
+        "|---|---|---|---|---|---|",
+    ]
+    for st in stats:
+        lines.append(f"| `{st['Name']}` | {st['Calls']} | {float(st['AverageNs']):.0f} | "
+                     f"{float(st['MinNs']):.0f} | {float(st['MaxNs']):.0f} | {float(st['StdDev']):.0f} |")
+    lines += [
+        "",
+        "Timed region (dispatches " + f"{first} .. {first + r['steps'] - 1} of each kernel): "
+        + "; ".join(parts) + ".",
+        "",
+        f"Same run, HIP events on the launch stream around the {r['steps']} timed calls: {ev_ns:.0f} ns per call, "
+        f"{r['value']} {r['unit']} ({100 * rf['frac']:.1f}% of {rf['peak']} {rf['unit']}); graphics clock "
+        f"median {rf.get('gfx_clock_mhz_median')} MHz, socket power median "
+        f"{rf.get('socket_power_w_median')} W (per-call window after the timed region).  Trace average "
+        f"(sum over the call's kernels) / event average = {total / ev_ns:.3f}.",
+        "",
+    ]
+    os.makedirs(PROFILES, exist_ok=True)
+    path = os.path.join(PROFILES, f"kernel_trace_{workload}.md")
     with open(path, "w") as f:
         f.write("\n".join(lines))
     return path
@@ -416,6 +493,9 @@ def main():
                          "let the GPU clock reach its loaded steady state")
     ap.add_argument("--settle", type=float, default=SETTLE_S,
                     help="seconds of untimed calls before the warm-up steps (clock settling)")
+    ap.add_argument("--dist", type=float, default=DIST_S,
+                    help="seconds of per-call timing after the timed region (the clock and power "
+                         "are read there; 0 = 20 calls)")
     ap.add_argument("--workload", default=None)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle time for cpu_baseline (0 = skip)")
@@ -427,12 +507,18 @@ def main():
                          "resident workgroups (0 = one per CU)")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic_<workload>.md from two rocprofv3 --pmc runs")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_LOG"),
+                    help="write profiles/kernel_trace_<workload>.md from a rocprofv3 --kernel-trace "
+                         "--stats run of bench.py and that run's output")
     args = ap.parse_args()
 
     from io_aware_tiled_08_amd import workloads as W
     name = args.workload or W.HEADLINE
     if args.summarize_traffic:
         print(summarize_traffic(*args.summarize_traffic, name))
+        return
+    if args.summarize_trace:
+        print(summarize_trace(*args.summarize_trace, name))
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the forward pass "
@@ -541,7 +627,7 @@ def main():
     # after the timed region, so the extra event records do not perturb it;
     # calls continue for at least DIST_S so that the graphics clock, sampled
     # every 10 ms, is read over a window of this kernel's sustained load.
-    n_dist = min(2000, max(20, int(DIST_S / max(ms * 1e-3, 1e-6))))
+    n_dist = min(2000, max(20, int(args.dist / max(ms * 1e-3, 1e-6))))
     pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
              for _ in range(n_dist)]
     t_d = time.perf_counter()
@@ -550,7 +636,7 @@ def main():
         step()
         b.record(stream)
     torch.cuda.synchronize()
-    while time.perf_counter() - t_d < DIST_S:
+    while time.perf_counter() - t_d < args.dist:
         for _ in range(10):
             step()
         torch.cuda.synchronize()

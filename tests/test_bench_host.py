@@ -117,3 +117,30 @@ def test_oracle_pool_stops_starting_units_after_the_budget():
     # at least one unit, even with no budget
     total, n, _, _ = bench.run_oracle_pool(range(5), run, 0.0)
     assert n >= 1
+
+
+def test_trace_summary_averages_the_timed_dispatches(tmp_path, monkeypatch):
+    """Dispatches are counted per kernel: the first (settle calls + warm-up)
+    are skipped, the next `steps` are the timed region."""
+    import json
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    d = tmp_path / "trace" / "host"
+    d.mkdir(parents=True)
+    name = "_ZN2fa_fwd_f16_persistent_kernel"
+    with open(d / "trace_kernel_stats.csv", "w") as f:
+        f.write('"Name","Calls","TotalDurationNs","AverageNs","Percentage","MinNs","MaxNs","StdDev"\n')
+        f.write(f'"{name}",30,0,150,100,100,300,10\n')
+    with open(d / "trace_kernel_trace.csv", "w") as f:
+        f.write("Kernel_Name,Start_Timestamp,End_Timestamp\n")
+        for i in range(30):  # 10 settle + 5 warm-up at 100 ns, 10 timed at 200 ns, 5 more at 300 ns
+            dur = 100 if i < 15 else (200 if i < 25 else 300)
+            f.write(f"{name},{1000 * i},{1000 * i + dur}\n")
+    log = tmp_path / "bench.log"
+    rec = {"value": 1.0, "unit": "TFLOP/s", "steps": 10, "warmup": 5,
+           "clock_settle": {"calls": 10},
+           "roofline": {"kernel_ms": 0.0002, "frac": 0.5, "peak": 2.0, "unit": "TFLOP/s"}}
+    log.write_text("noise\n" + json.dumps(rec) + "\n")
+    path = bench.summarize_trace(str(tmp_path / "trace"), str(log), "headline_f16_d128")
+    text = open(path).read()
+    assert "200 ns over 10 dispatches" in text
+    assert "event average = 1.000" in text
