@@ -53,7 +53,7 @@ KERNEL_SOURCES = {
 # (dominant kernel, every kernel of one call) name patterns in rocprofv3 output
 KERNEL_NAME_PATTERN = {"f16": ("fwd_f16_", "fwd_f16_"),
                        "bf16": ("fwd_f16_", "fwd_f16_"),
-                       "f32": ("fwd_f32_kernel", "fwd_f32_kernel"),
+                       "f32": ("fwd_f32_", "fwd_f32_"),
                        "kvcache": ("kvcache_fwd_kernel", "kvcache_"),
                        "fp8": ("fwd_fp8_kernel", "fwd_fp8_kernel"),
                        "bwd": ("bwd_dkdv_kernel", "bwd_")}

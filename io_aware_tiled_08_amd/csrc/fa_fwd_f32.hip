@@ -19,6 +19,7 @@
 // Each wave reads its K and V tiles straight from global memory into
 // registers (no tile is shared between waves); Q is staged once in LDS.
 #include "fa_device.h"
+#include "fa_f16_common.h"
 #include "fa_launch.h"
 
 namespace fa {
@@ -221,6 +222,243 @@ __global__ void __launch_bounds__(F32Lds<D>::kWaves * 64, 1) fwd_f32_kernel(Kern
   }
 }
 
+// ---------------------------------------------------------------------------
+// Small fp32 problems at d = 64 (few 32-row blocks, e.g. one head of 512
+// queries): a workgroup owns only 4 query rows, so the launch spreads over
+// eight times as many CUs, and its 4 waves take every 4th chunk of 64 keys.
+//
+// v_mfma_f32_4x4x1_16b_f32 computes 16 independent 4x4 blocks; lane 4b + i
+// supplies row i of block b's A column, lane 4b + j column j of its B row,
+// and register r of lane 4b + j receives D[b][r][j].
+//   Scores:  block b = keys 4b .. 4b+3 of the chunk, columns = the 4 queries.
+//            Lane l supplies its own key row K[k0 + l][c] as A and its query's
+//            row Q[q0 + l%4][c] as B; after the D products over c, register r
+//            of lane 4b + j holds the score of key 4b + r against query j.
+//   P V:     product (r, c) takes block b's key 4b + r: B is register r of
+//            the weights (the lane's own query j), A in lane 4b + i is
+//            V[k0 + 4b + r][16 i + c].  Register i of lane 4b + j then sums
+//            V[.][16 i + c] P[j][.] over block b's keys: a partial O for query
+//            j, summed over the 16 blocks (and the waves) at the end.
+// The online softmax is the 32-row kernel's: running max (in log2 units)
+// over the chunk, reduced across the 16 lanes of a query, rescale by
+// exp2(m_old - m_new); each lane keeps a partial sum of its own weights.
+// Each wave sums its lanes' partial O over the 16 blocks (cross-lane), and
+// the waves' (O, m, l) are merged through LDS with weights 2^(m_w - M).
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+constexpr int kQ4Rows = 4;
+constexpr int kQ4Keys = 64;
+constexpr int kQ4Waves = 4;
+
+// Maximum or sum over the 16 lanes of one query (lanes congruent mod 4):
+// row rotations by 4 and 8 within each 16-lane row, then the row pairs
+// (permlane16 swap) and the halves (permlane32 swap).
+template <typename Op>
+__device__ __forceinline__ float query_reduce(float x, Op op) {
+  x = op(x, bits<float>(__builtin_amdgcn_update_dpp(0, bits<int>(x), 0x124, 0xF, 0xF, false)));
+  x = op(x, bits<float>(__builtin_amdgcn_update_dpp(0, bits<int>(x), 0x128, 0xF, 0xF, false)));
+  const auto r16 = __builtin_amdgcn_permlane16_swap(bits<uint32_t>(x), bits<uint32_t>(x), false, false);
+  x = op(bits<float>(r16[0]), bits<float>(r16[1]));
+  const auto r32 = __builtin_amdgcn_permlane32_swap(bits<uint32_t>(x), bits<uint32_t>(x), false, false);
+  return op(bits<float>(r32[0]), bits<float>(r32[1]));
+}
+
+template <bool CAUSAL>
+__global__ void __launch_bounds__(kQ4Waves * 64, 1) fwd_f32_q4_kernel(KernelParams p) {
+  constexpr int D = 64;
+  constexpr int RB = D * 4;              // bytes per K or V row
+  constexpr int CH = kQ4Keys * RB;       // bytes of one chunk of K (or V)
+  // Each wave stages its chunk of K and of V in its own LDS area; after the
+  // loop the same LDS holds the waves' partial O for the merge.
+  __shared__ __attribute__((aligned(1024))) char smem[kQ4Waves][2][CH];
+  static_assert(sizeof(float) * kQ4Waves * 64 * 16 * 4 <= sizeof(smem), "merge area");
+  float(*part)[64][16][4] = (float(*)[64][16][4])&smem[0][0][0];  // [wave][lane][c][i]
+  __shared__ float m_lds[kQ4Waves][kQ4Rows], l_lds[kQ4Waves][kQ4Rows];
+
+  const int64_t N = p.N;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 3;   // query of the lane (B column / output column) and A row
+  const int b = lane >> 2;  // MFMA block
+  const int64_t bh = blockIdx.x / p.n_qblk;
+  int qblk = (int)(blockIdx.x % p.n_qblk);
+  if (CAUSAL) qblk = p.n_qblk - 1 - qblk;  // longest blocks first
+  const int64_t q0 = (int64_t)qblk * kQ4Rows;
+  const int64_t qj = q0 + j;
+
+  const float* __restrict__ Qh = (const float*)p.q + bh * N * D;
+  const float* __restrict__ Kh = (const float*)p.k + bh * N * D;
+  const float* __restrict__ Vh = (const float*)p.v + bh * N * D;
+
+  const int64_t kv_end = CAUSAL ? (q0 + kQ4Rows < N ? q0 + kQ4Rows : N) : N;
+  const int n_chunks = (int)((kv_end + kQ4Keys - 1) / kQ4Keys);
+  const float c = p.c;
+
+  // Rows at or past N read as zeros (the buffer resources end there).
+  auto rows_rsrc = [&](const float* head, int64_t r0) {
+    const int64_t rows = N - r0 < 0 ? 0 : N - r0;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(head + r0 * D), (short)0,
+                                             (int)(rows * D * 4), 0x00020000);
+  };
+  auto load16 = [](float* dst, __amdgpu_buffer_rsrc_t rs, int off, uint32_t flip) {
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0) ^ flip;
+    dst[0] = bits<float>(x[0]);
+    dst[1] = bits<float>(x[1]);
+    dst[2] = bits<float>(x[2]);
+    dst[3] = bits<float>(x[3]);
+  };
+  // Chunk ch goes to this wave's LDS area by direct-to-LDS loads, read
+  // coalesced (piece pc covers rows 4 pc .. 4 pc + 3; lane i fills LDS chunk
+  // slot i % 16 of row 4 pc + i / 16).  Each row's 16-byte chunks are stored
+  // permuted so the operand reads below hit every bank group: chunk s of K row
+  // r at slot s ^ (r & 15) (lane l reads row l), chunk s of V row r at slot
+  // s ^ ((r >> 2) & 3) (16 lanes read rows 4b + r for four b, chunks 4i + k for
+  // four i).  The permutation is applied on the global side.
+  const uint32_t lds_k = lds_addr(&smem[wave][0][0]);
+  const uint32_t lds_v = lds_addr(&smem[wave][1][0]);
+  const int prow = lane >> 4, slot = lane & 15;  // row within a piece, LDS slot
+  auto issue_chunk = [&](int ch) {
+    const int64_t k0 = (int64_t)ch * kQ4Keys;
+    const int64_t rows = N - k0 < kQ4Keys ? N - k0 : kQ4Keys;
+    const u32x4 rk = buffer_rsrc(Kh + k0 * D, (uint32_t)(rows * RB));
+    const u32x4 rv = buffer_rsrc(Vh + k0 * D, (uint32_t)(rows * RB));
+    // Nothing may still read this area when the pieces start landing.
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+#pragma unroll
+    for (int pc = 0; pc < CH / 1024; ++pc) {
+      const int r = 4 * pc + prow;
+      dma_load16(rk, lds_k + pc * 1024, r * RB + (slot ^ (r & 15)) * 16);
+      dma_load16(rv, lds_v + pc * 1024, r * RB + (slot ^ ((r >> 2) & 3)) * 16);
+    }
+  };
+  // This lane's K row (key 64 ch + lane, all D values) and the V values it
+  // feeds as A operand (rows 4b .. 4b+3, columns 16 j .. 16 j + 15).
+  auto read_chunk = [&](float* kf, float* vf) {
+    const char* kl = &smem[wave][0][0];
+    const char* vl = &smem[wave][1][0];
+#pragma unroll
+    for (int sc = 0; sc < D / 4; ++sc) {
+      const float4 x = *(const float4*)(kl + lane * RB + (sc ^ (lane & 15)) * 16);
+      kf[4 * sc] = x.x;
+      kf[4 * sc + 1] = x.y;
+      kf[4 * sc + 2] = x.z;
+      kf[4 * sc + 3] = x.w;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int row = 4 * b + r;
+        const float4 x = *(const float4*)(vl + row * RB + ((4 * j + k) ^ (b & 3)) * 16);
+        vf[16 * r + 4 * k] = x.x;
+        vf[16 * r + 4 * k + 1] = x.y;
+        vf[16 * r + 4 * k + 2] = x.z;
+        vf[16 * r + 4 * k + 3] = x.w;
+      }
+  };
+
+  f32x4 acc[16];
+#pragma unroll
+  for (int cc = 0; cc < 16; ++cc) acc[cc] = f32x4{};
+  float m = kNegInf, lpart = 0.f;
+
+  // The first chunk's loads go out before Q's, so the two latencies overlap.
+  if (wave < n_chunks) issue_chunk(wave);
+  float qf[D];
+  {
+    const auto rs = rows_rsrc(Qh, q0);
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i) load16(qf + 4 * i, rs, (j * D + 4 * i) * 4, p.q_sign);
+  }
+
+  auto compute = [&](const float* kf, const float* vf, int ch) {
+    const int64_t k0 = (int64_t)ch * kQ4Keys;
+    // Four independent accumulators (d mod 4), summed at the end.
+    f32x4 sp[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};
+#pragma unroll
+    for (int cc = 0; cc < D; ++cc) sp[cc & 3] = __builtin_amdgcn_mfma_f32_4x4x1f32(kf[cc], qf[cc], sp[cc & 3], 0, 0, 0);
+    f32x4 s = (sp[0] + sp[1]) + (sp[2] + sp[3]);
+    // Key 4b + r of the chunk against query qj; past N or after the query
+    // (causal) it is invisible.
+    float mx = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t key = k0 + 4 * b + r;
+      if (key >= N || (CAUSAL && key > qj)) s[r] = kNegInf;
+      mx = fmaxf(mx, s[r]);
+    }
+    mx = query_reduce(mx, [](float x, float y) { return fmaxf(x, y); });
+    const float mxc = mx == kNegInf ? kNegInf : mx * c;
+    const float m_new = fmaxf(m, mxc);
+    const float m_use = m_new == kNegInf ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m - m_use);
+    m = m_new;
+    float pw[4];
+    float rs = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pw[r] = s[r] == kNegInf ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -m_use));
+      rs += pw[r];
+    }
+    lpart = lpart * alpha + rs;
+#pragma unroll
+    for (int cc = 0; cc < 16; ++cc) acc[cc] *= alpha;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int cc = 0; cc < 16; ++cc)
+        acc[cc] = __builtin_amdgcn_mfma_f32_4x4x1f32(vf[16 * r + cc], pw[r], acc[cc], 0, 0, 0);
+  };
+
+  // Chunks wave, wave + 4, ...: once a chunk's operands are in registers the
+  // next chunk's loads go out, then the products run.
+  for (int ch = wave; ch < n_chunks; ch += kQ4Waves) {
+    float kf[D], vf[64];
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's pieces have landed
+    read_chunk(kf, vf);
+    if (ch + kQ4Waves < n_chunks) issue_chunk(ch + kQ4Waves);
+    compute(kf, vf, ch);
+  }
+  __syncthreads();  // every wave is done with its LDS area
+
+  // Merge: each wave sums its partial O over the 16 blocks in registers; the
+  // lanes of block 0 then hold the wave's O for their query, which goes to LDS
+  // with the wave's maximum and sum.
+  const auto add = [](float x, float y) { return x + y; };
+  const float lq = query_reduce(lpart, add);
+#pragma unroll
+  for (int cc = 0; cc < 16; ++cc)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[cc][i] = query_reduce(acc[cc][i], add);
+  if (lane < kQ4Rows) {
+#pragma unroll
+    for (int cc = 0; cc < 16; ++cc)
+      *(float4*)&part[wave][lane][cc][0] = make_float4(acc[cc][0], acc[cc][1], acc[cc][2], acc[cc][3]);
+    m_lds[wave][lane] = m;
+    l_lds[wave][lane] = lq;
+  }
+  __syncthreads();
+  if (tid < kQ4Rows * D) {
+    const int q = tid >> 6, d = tid & 63;  // one output element per thread
+    const int64_t qi = q0 + q;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kQ4Waves; ++w) M = fmaxf(M, m_lds[w][q]);
+    const float M_use = M == kNegInf ? 0.f : M;
+    float L = 0.f, o = 0.f;
+#pragma unroll
+    for (int w = 0; w < kQ4Waves; ++w) {
+      const float wt = __builtin_amdgcn_exp2f(m_lds[w][q] - M_use);
+      L += wt * l_lds[w][q];
+      o += wt * part[w][q][d & 15][d >> 4];
+    }
+    if (qi < N) {
+      ((float*)p.o)[(bh * N + qi) * D + d] = o / L;
+      if (d == 0) p.lse[bh * N + qi] = (M + __builtin_amdgcn_logf(L)) * kLn2;
+    }
+  }
+}
+
 template <int D, bool CAUSAL>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   static_assert(kRows == kRowsPerWorkgroupF32, "rows per workgroup");
@@ -240,9 +478,28 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <bool CAUSAL>
+hipError_t launch_q4(const FwdArgs& a, hipStream_t stream) {
+  KernelParams p;
+  p.q = a.q;
+  p.k = a.k;
+  p.v = a.v;
+  p.o = a.o;
+  p.lse = a.lse;
+  p.N = a.N;
+  p.n_qblk = (int32_t)((a.N + kQ4Rows - 1) / kQ4Rows);
+  p.c = __builtin_fabsf(a.scale) * kLog2e;
+  p.q_sign = a.scale < 0.f ? 0x80000000u : 0u;
+  hipLaunchKernelGGL((fwd_f32_q4_kernel<CAUSAL>), dim3((unsigned)(a.BH * p.n_qblk)),
+                     dim3(kQ4Waves * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_forward_f32(const FwdArgs& a, hipStream_t stream) {
+  if (use_f32_q4(a.d, a.BH, a.N))
+    return a.causal ? launch_q4<true>(a, stream) : launch_q4<false>(a, stream);
   if (a.d == 64) return a.causal ? launch<64, true>(a, stream) : launch<64, false>(a, stream);
   return a.causal ? launch<128, true>(a, stream) : launch<128, false>(a, stream);
 }

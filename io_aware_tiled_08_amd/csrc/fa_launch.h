@@ -49,6 +49,15 @@ hipError_t launch_forward_f16_persistent(const FwdArgs& a, int n_wg, hipStream_t
 // take alternate key tiles; for causal problems with few 256-row blocks.
 hipError_t launch_forward_f16_keysplit(const FwdArgs& a, hipStream_t stream);
 
+// Whether an fp32 problem runs on the 4-row kernel (fwd_f32_q4_kernel):
+// d = 64 and a small problem, where one workgroup per 32-row block would
+// leave most CUs idle.  Every 4-row workgroup reads all of its head's K and V
+// (N * 512 bytes), B*H*N/4 workgroups in all, so the limit on B*H*N^2 keeps
+// that re-reading from L2 small (one head of 512 queries reads 32 MiB).
+inline bool use_f32_q4(int d, int64_t BH, int64_t N) {
+  return d == 64 && N <= 4096 && BH * N * N <= ((int64_t)1 << 20);
+}
+
 // Whether flash_attn_fwd uses the key-split schedule: causal, d = 64, and at
 // most two 256-row blocks per CU of the MI355X (256 CUs), where the
 // longest-first dispatch of 256-row blocks leaves CUs idle.

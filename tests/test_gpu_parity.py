@@ -296,3 +296,18 @@ def test_graph_capture_replays(B, H, N, causal):
         o2, _ = gpu_forward(q[:, :1].contiguous(), k[:, :1].contiguous(), v[:, :1].contiguous(),
                             scale, causal)
         assert torch.equal(o2, o_ref[:, :1])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,N", [
+    (1, 1, 2100),  # B*H*N^2 over 2^20: the 32-row kernel
+    (2, 8, 300),   # B*H*N^2 = 1.44e7: the 32-row kernel
+    (4, 1, 512),   # B*H*N^2 = 2^20 (the limit): the 4-row kernel
+    (1, 3, 37),    # ragged 4-row blocks
+])
+def test_f32_both_schedules(B, H, N, causal):
+    """fp32 at d=64 runs on 4-row workgroups when B*H*N^2 <= 2^20, else on
+    32-row workgroups; both against the oracle at 1e-5."""
+    q, k, v = W.random_qkv(B, H, N, 64, "f32", seed=3300 + N)
+    o, lse = gpu_forward(q, k, v, 0.125, causal)
+    check(o, lse, q, k, v, 0.125, causal, "f32", label=f"f32 B={B} H={H} N={N} causal={causal}")
