@@ -275,6 +275,106 @@ def summarize_traffic(fetch_csv: str, write_csv: str, workload: str) -> str:
     return path
 
 
+SQ_PASSES = (
+    "SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_INSTS_SALU SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS "
+    "SQ_WAIT_ANY SQ_WAIT_INST_ANY GRBM_GUI_ACTIVE",
+    "SQ_INST_LEVEL_LDS SQ_INSTS_LDS_LOAD_BANDWIDTH SQ_LDS_IDX_ACTIVE SQ_BUSY_CYCLES SQ_ACTIVE_INST_ANY "
+    "SQ_ACTIVE_INST_SCA SQ_VALU_MFMA_BUSY_CYCLES SQ_WAVE_CYCLES GRBM_GUI_ACTIVE",
+    "SQ_VALU_MFMA_COEXEC_CYCLES SQ_WAIT_INST_LDS SQ_INSTS_VALU_TRANS_F32 SQ_INSTS_VALU_CVT SQ_INSTS_SMEM "
+    "SQ_INSTS_VMEM SQ_LDS_ADDR_CONFLICT SQ_LDS_UNALIGNED_STALL GRBM_GUI_ACTIVE",
+)
+N_XCD, N_CU, N_SIMD = 8, 256, 1024
+
+
+SQ_UNITS = (
+    "GRBM_GUI_ACTIVE is summed over the 8 XCDs, so one XCD's busy cycles are GRBM_GUI_ACTIVE / 8 "
+    "(in a counter run that also holds the dispatch's own set-up, so fractions over it are lower "
+    "bounds).  SQ_WAVE_CYCLES, SQ_WAIT_* and SQ_ACTIVE_INST_* count quad-cycles (4 cycles); "
+    "SQ_VALU_MFMA_BUSY_CYCLES and SQ_VALU_MFMA_COEXEC_CYCLES count cycles per SIMD, summed over the "
+    "1024 SIMDs; SQ_INSTS_VALU includes the MFMA instructions; SQ_INSTS_LDS_LOAD_BANDWIDTH counts "
+    "64-byte units.")
+
+
+def summarize_counters(csvs, workload: str) -> str:
+    """Turns the three SQ counter passes (rocprofv3 --pmc with the counter
+    sets of SQ_PASSES, one run of bench.py each) into
+    profiles/sq_counters_<workload>.md: per kernel of the workload, the mean
+    of each counter per dispatch and the ratios read from them (units as
+    SQ_UNITS states)."""
+    w, key = workload_by_name(workload)
+    _, all_pat = KERNEL_NAME_PATTERN[key]
+    vals = {}
+    for path in csvs:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if all_pat in r["Kernel_Name"]:
+                    vals.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(
+                        float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no dispatches of {all_pat}* in {csvs}")
+    lines = [
+        f"# SQ counters, workload {workload}",
+        "",
+        f"Workload: {w.description}.",
+        "",
+        "Commands (GPU host; R = the repository root; rocprofv3 run from /tmp with TMPDIR=/tmp),",
+        "one run per counter set, at most 8 SQ counters each:",
+        "",
+    ]
+    for i, counters in enumerate(SQ_PASSES, 1):
+        lines += [f"    rocprofv3 --pmc {counters} \\",
+                  f"        -f csv -d $R/gpurun_out/sq_{workload}/p{i} -o p -- python3 $R/bench.py --workload {workload} "
+                  "--steps 5 --warmup 2 --settle 0 --dist 0 --cpu-budget 0"]
+    lines += [f"    python3 bench.py --workload {workload} --summarize-counters "
+              + " ".join(f"gpurun_out/sq_{workload}/p{i}/p_counter_collection.csv" for i in (1, 2, 3)),
+              "", "Units: " + SQ_UNITS, ""]
+    for name, c in sorted(vals.items()):
+        m = {k: sum(v) / len(v) for k, v in c.items()}
+        lines += [f"## `{name[:110]}`", "", "| counter | mean per dispatch | dispatches |", "|---|---|---|"]
+        lines += [f"| {k} | {m[k]:.4g} | {len(c[k])} |" for k in sorted(m)]
+        g = lambda k: m.get(k)  # noqa: E731
+        derived = []
+        if g("GRBM_GUI_ACTIVE"):
+            length = g("GRBM_GUI_ACTIVE") / N_XCD
+            derived.append(f"busy length (GRBM_GUI_ACTIVE / {N_XCD}): {length:.0f} cycles")
+            if g("SQ_VALU_MFMA_BUSY_CYCLES") is not None:
+                derived.append("matrix pipe busy per SIMD over that length: "
+                               f"{g('SQ_VALU_MFMA_BUSY_CYCLES') / (length * N_SIMD):.1%}")
+        if g("SQ_VALU_MFMA_COEXEC_CYCLES") is not None and g("SQ_VALU_MFMA_BUSY_CYCLES"):
+            derived.append("vector instructions issued while the matrix pipe is busy / matrix busy: "
+                           f"{g('SQ_VALU_MFMA_COEXEC_CYCLES') / g('SQ_VALU_MFMA_BUSY_CYCLES'):.1%}")
+        wave = g("SQ_WAVE_CYCLES")
+        if wave:
+            for k, label in (("SQ_WAIT_ANY", "wave time at a wait-count instruction"),
+                             ("SQ_WAIT_INST_ANY", "wave time with an instruction ready but not issued"),
+                             ("SQ_WAIT_INST_LDS", "wave time waiting to issue an LDS instruction")):
+                if g(k) is not None:
+                    derived.append(f"{label} ({k} / SQ_WAVE_CYCLES): {g(k) / wave:.1%}")
+        if g("SQ_ACTIVE_INST_VALU") and g("SQ_INSTS_VALU"):
+            derived.append("cycles per vector instruction (4 x SQ_ACTIVE_INST_VALU / SQ_INSTS_VALU): "
+                           f"{4 * g('SQ_ACTIVE_INST_VALU') / g('SQ_INSTS_VALU'):.2f}")
+        if g("SQ_INSTS_LDS_LOAD_BANDWIDTH") is not None and g("SQ_LDS_IDX_ACTIVE"):
+            b = 64 * g("SQ_INSTS_LDS_LOAD_BANDWIDTH")
+            derived.append(f"LDS bytes read: {b:.4g}; per LDS-active cycle and CU: "
+                           f"{b / g('SQ_LDS_IDX_ACTIVE'):.0f}")
+        if key in ("f16", "bf16") and not w.causal and "fwd_f16_" in name and g("SQ_INSTS_MFMA"):
+            # one wave-tile = 32 query rows of one wave against one 128-key tile
+            n_wt = w.B * w.H * ((w.N + 31) // 32) * ((w.N + 127) // 128)
+            per = ", ".join(f"{label} {x / n_wt:.1f}" for label, x in (
+                ("vector (not MFMA)", g("SQ_INSTS_VALU") - g("SQ_INSTS_MFMA")),
+                ("MFMA", g("SQ_INSTS_MFMA")), ("of them exp", g("SQ_INSTS_VALU_TRANS_F32")),
+                ("conversions", g("SQ_INSTS_VALU_CVT")), ("LDS", g("SQ_INSTS_LDS")),
+                ("scalar", g("SQ_INSTS_SALU")), ("vector memory", g("SQ_INSTS_VMEM")))
+                if x is not None)
+            derived.append(f"instructions per wave-tile (32 rows x 128 keys, {n_wt} per dispatch): {per}")
+        lines += ["", "Read from them:", ""] + [f"- {x}" for x in derived] + [""]
+    os.makedirs(PROFILES, exist_ok=True)
+    path = os.path.join(PROFILES, f"sq_counters_{workload}.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines))
+    return path
+
+
 def summarize_trace(trace_dir: str, bench_log: str, workload: str) -> str:
     """Turns one `rocprofv3 --kernel-trace --stats -f csv` run of bench.py
     (its output directory and the run's stdout) into
@@ -442,6 +542,69 @@ class ClockSampler:
         return [x for t, x in (self.power if power else self.samples) if t0 <= t <= t1]
 
 
+def calibrate(seconds: float = 1.5) -> None:
+    """Reachable fp16 matrix throughput on this card, with the clock and socket
+    power held under it: hipBLASLt square GEMMs (torch.matmul, n = 8192 and
+    16384) and a register-only chain of 32x32x16 f16 MFMAs (libfa_calib.so,
+    256 workgroups x 8 waves x 4 chains).  Prints one JSON line per case.  The
+    attention kernel's roofline fraction is quoted against the published dense
+    peak; these lines say how much of that peak the card sustains at all
+    under its power limit."""
+    import ctypes
+
+    import torch
+
+    from io_aware_tiled_08_amd.build import CALIB_LIB_PATH, build_calibration_library
+    if not os.path.exists(CALIB_LIB_PATH):
+        build_calibration_library()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+
+    def measure(label, fn, reps, flops):
+        t = time.perf_counter()
+        while time.perf_counter() - t < seconds:  # clock settling
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+        clk = ClockSampler()
+        clk.start()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        s.record(stream)
+        for _ in range(reps):
+            fn()
+        e.record(stream)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        clk.stop()
+        ms = s.elapsed_time(e) / reps
+        tf = flops / (ms * 1e-3) / 1e12
+        mhz = sorted(clk.window(t0, t1))
+        watts = sorted(clk.window(t0, t1, power=True))
+        print(json.dumps({"calibration": label, "ms": round(ms, 4), "tflops": round(tf, 1),
+                          "frac_of_peak": round(tf / MFMA_PEAK_TFLOPS["f16"], 4),
+                          "clock_mhz_median": percentile(mhz, 0.5) if mhz else None,
+                          "socket_power_w_median": percentile(watts, 0.5) if watts else None,
+                          "samples": len(mhz), "window_s": round(t1 - t0, 3)}), flush=True)
+
+    for n, reps in ((8192, 400), (16384, 50)):
+        a = torch.randn(n, n, device=dev, dtype=torch.float16)
+        b = torch.randn(n, n, device=dev, dtype=torch.float16)
+        c = torch.empty(n, n, device=dev, dtype=torch.float16)
+        measure(f"gemm_f16_n{n}", lambda: torch.matmul(a, b, out=c), reps, 2.0 * n ** 3)
+        del a, b, c
+    lib = ctypes.CDLL(CALIB_LIB_PATH)
+    lib.fa_calib_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    blocks, iters = 256, 20000
+    out = torch.empty(blocks * 512, device=dev)
+
+    def chain():
+        rc = lib.fa_calib_mfma(out.data_ptr(), blocks, iters, stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"fa_calib_mfma failed ({rc})")
+    measure("mfma_chain_f16_32x32x16", chain, 20, float(blocks) * 8 * 4 * iters * 32768)
+
+
 def cpu_baseline_cache(w, q, k, v, budget_s: float):
     """Times the fp64 oracle on a key/value-cache workload, whole (b, h) heads
     on a thread pool over the host's cores until the budget is spent; the rate
@@ -505,8 +668,13 @@ def main():
     ap.add_argument("--persistent", type=int, default=None, metavar="NWG",
                     help="run an fp16/bf16 forward workload on the persistent schedule with NWG "
                          "resident workgroups (0 = one per CU)")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="print the card's sustained fp16 GEMM and register-only MFMA throughput "
+                         "with clock and power, then exit")
     ap.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic_<workload>.md from two rocprofv3 --pmc runs")
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("P1_CSV", "P2_CSV", "P3_CSV"),
+                    help="write profiles/sq_counters_<workload>.md from the three SQ counter passes")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "BENCH_LOG"),
                     help="write profiles/kernel_trace_<workload>.md from a rocprofv3 --kernel-trace "
                          "--stats run of bench.py and that run's output")
@@ -519,6 +687,12 @@ def main():
         return
     if args.summarize_trace:
         print(summarize_trace(*args.summarize_trace, name))
+        return
+    if args.summarize_counters:
+        print(summarize_counters(args.summarize_counters, name))
+        return
+    if args.calibrate:
+        calibrate()
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the forward pass "

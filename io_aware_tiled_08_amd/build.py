@@ -60,5 +60,21 @@ def build_library(verbose: bool = False, extra_flags=()) -> str:
     return LIB_PATH
 
 
+CALIB_SOURCE = "calib_mfma.hip"
+CALIB_LIB_PATH = os.path.join(PKG, "libfa_calib.so")
+
+
+def build_calibration_library(verbose: bool = False) -> str:
+    """Compile the roofline calibration kernel (bench.py --calibrate) into its
+    own small library, separate from the attention library."""
+    tmp = CALIB_LIB_PATH + ".tmp"
+    _run([hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          os.path.join(CSRC, CALIB_SOURCE), "-o", tmp], verbose)
+    os.replace(tmp, CALIB_LIB_PATH)
+    return CALIB_LIB_PATH
+
+
 if __name__ == "__main__":
     print(build_library(verbose=True))
+    print(build_calibration_library(verbose=True))

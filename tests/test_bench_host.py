@@ -144,3 +144,36 @@ def test_trace_summary_averages_the_timed_dispatches(tmp_path, monkeypatch):
     text = open(path).read()
     assert "200 ns over 10 dispatches" in text
     assert "event average = 1.000" in text
+
+
+def test_counter_summary_reads_units_and_per_tile_counts(tmp_path, monkeypatch):
+    """GRBM_GUI_ACTIVE is divided by the 8 XCDs, the matrix-busy cycles by the
+    1024 SIMDs, quad-cycle wait counters by quad-cycle wave cycles, and the
+    forward's instruction counts by its wave-tiles (32 rows x 128 keys)."""
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    name = "_ZN2fa_fwd_f16_persistent_kernel"
+    w = W.WORKLOADS["headline_f16_d128"]
+    n_wt = w.B * w.H * (w.N // 32) * (w.N // 128)
+    length = 400000
+    values = {"GRBM_GUI_ACTIVE": 8 * length, "SQ_VALU_MFMA_BUSY_CYCLES": 0.5 * length * 1024,
+              "SQ_VALU_MFMA_COEXEC_CYCLES": 0.25 * length * 1024, "SQ_WAVE_CYCLES": 1000.0,
+              "SQ_WAIT_INST_LDS": 100.0, "SQ_INSTS_VALU": 300.0 * n_wt, "SQ_INSTS_MFMA": 80.0 * n_wt,
+              "SQ_ACTIVE_INST_VALU": 300.0 * n_wt}
+    paths = []
+    for i, chunk in enumerate((list(values)[:3], list(values)[3:6], list(values)[6:])):
+        p = tmp_path / f"p{i}.csv"
+        with open(p, "w") as f:
+            f.write("Kernel_Name,Counter_Name,Counter_Value\n")
+            for c in chunk:
+                for _ in range(2):
+                    f.write(f"{name},{c},{values[c]}\n")
+                f.write(f"other_kernel,{c},1\n")
+        paths.append(str(p))
+    text = open(bench.summarize_counters(paths, "headline_f16_d128")).read()
+    assert "busy length (GRBM_GUI_ACTIVE / 8): 400000 cycles" in text
+    assert "matrix pipe busy per SIMD over that length: 50.0%" in text
+    assert "while the matrix pipe is busy / matrix busy: 50.0%" in text
+    assert "waiting to issue an LDS instruction (SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES): 10.0%" in text
+    assert "cycles per vector instruction (4 x SQ_ACTIVE_INST_VALU / SQ_INSTS_VALU): 4.00" in text
+    assert "vector (not MFMA) 220.0, MFMA 80.0" in text
+    assert "other_kernel" not in text
