@@ -668,6 +668,9 @@ def main():
     ap.add_argument("--persistent", type=int, default=None, metavar="NWG",
                     help="run an fp16/bf16 forward workload on the persistent schedule with NWG "
                          "resident workgroups (0 = one per CU)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the steps as one captured HIP graph (square forward workloads): "
+                         "removes host launch gaps for kernels shorter than a launch")
     ap.add_argument("--calibrate", action="store_true",
                     help="print the card's sustained fp16 GEMM and register-only MFMA throughput "
                          "with clock and power, then exit")
@@ -703,6 +706,8 @@ def main():
     cache = key == "kvcache"
     if args.persistent is not None and key not in ("f16", "bf16"):
         raise SystemExit("--persistent applies to the fp16/bf16 forward workloads")
+    if args.graph and key not in ("f16", "bf16", "f32"):
+        raise SystemExit("--graph applies to the square forward workloads")
 
     import torch
 
@@ -785,13 +790,34 @@ def main():
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    graph = None
+    if args.graph:
+        # The timed steps as one HIP graph (captured on a side stream; the
+        # step closures read `stream`, so they launch onto the capture
+        # stream), replayed once: kernels back to back with no host launch
+        # gaps, for workloads whose kernel is shorter than a host launch.
+        launch_stream = stream
+        cap = torch.cuda.Stream(dev)
+        cap.wait_stream(launch_stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(cap):
+            stream = cap
+            with torch.cuda.graph(graph, stream=cap):
+                for _ in range(args.steps):
+                    step()
+        stream = launch_stream
+        graph.replay()  # one untimed replay
+        torch.cuda.synchronize()
     # HIP events recorded on the stream the kernels are launched on.
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     start.record(stream)
-    for _ in range(args.steps):
-        step()
+    if graph is not None:
+        graph.replay()
+    else:
+        for _ in range(args.steps):
+            step()
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -929,6 +955,7 @@ def main():
     result["device"] = {"name": props.name, "cus": props.multi_processor_count,
                         "arch": getattr(props, "gcnArchName", "")}
     result["timed_wall_s"] = round(wall, 4)
+    result["launch"] = "hip_graph" if graph is not None else "stream"
     result["clock_settle"] = {"seconds": round(settle_s, 2), "calls": settle_calls,
                               "note": "untimed calls before the warm-up steps"}
     if args.cpu_budget > 0:

@@ -30,10 +30,13 @@
 //     The CU's load path takes one 1 KiB piece per about 16 cycles and a wave
 //     issues in order, so a wave that issues a tile's pieces is held until
 //     they are accepted; the two tensors' loads are therefore split between
-//     the groups, each at the start of its own V phase: group B issues K two
-//     tiles ahead, group A issues V for the tile it is turning into P (that
-//     buffer's last reader finished two slots earlier) and waits for it
-//     before the barrier that ends the slot.  Each row's 16-byte chunks are
+//     the groups: group B issues K two tiles ahead at the start of its V
+//     phase, group A issues V for the tile it is about to turn into P (that
+//     buffer's last reader finished a slot earlier) and waits for it before
+//     the barrier that ends its V phase.  At d = 128 A issues at the start of
+//     its V phase; at d = 64, where the softmax phase is the longer of the
+//     two, A issues at the end of its M phase, in the time it would otherwise
+//     wait at the barrier.  Each row's 16-byte chunks are
 //     stored XOR-permuted so that the operand reads hit all LDS banks; the
 //     permutation is applied on the global side (lane i of a load always
 //     writes LDS bytes 16i..16i+15).
@@ -493,12 +496,14 @@ __device__ __forceinline__ void fwd_f16_tiles(const KernelParams& p, const WorkI
   // phases: group B issues K(t+2) at the start of slot 2t+2; it overwrites
   // K(t) (last read in slot 2t+1), is first read in slot 2t+4, and B waits
   // for it at the end of its next M phase (slot 2t+3).  Group A issues V(t)
-  // at the start of slot 2t+1; it overwrites V(t-2) (last read in slot 2t-1),
-  // is first read in slot 2t+2, and A waits for it at the end of that same V
-  // phase, before the barrier that closes slot 2t+1.  A wave works on
+  // at the start of slot 2t+1 (at d = 64: at the end of its M(t) in slot 2t,
+  // kEarlyV); it overwrites V(t-2) (last read in slot 2t-1), is first read in
+  // slot 2t+2, and A waits for it at the end of its V(t) phase, before the
+  // barrier that closes slot 2t+1.  A wave works on
   // tiles t < wave_tiles only (causal waves above the diagonal stop early)
   // but takes part in every slot's barrier.  The stream runs the same slots,
   // counted in stream steps instead of tiles.
+  constexpr bool kEarlyV = D == 64;
   auto iteration = [&](int t, auto mwork, auto vwork) {
     wave_priority<1>();
     mwork();
@@ -508,11 +513,12 @@ __device__ __forceinline__ void fwd_f16_tiles(const KernelParams& p, const WorkI
     for (int db = 0; db < ND; ++db) fence(o[db]);
     fence(lacc);
     wave_priority<0>();
+    if (kEarlyV && !group_b) issue_v(t);
     if (group_b) wait_loads();
     barrier();
     if (group_b)
       issue_k(t + 2);
-    else
+    else if (!kEarlyV)
       issue_v(t);
     vwork();
     if (!group_b) wait_loads();
