@@ -396,7 +396,9 @@ def summarize_trace(trace_dir: str, bench_log: str, workload: str) -> str:
     trace = [r for r in csv.DictReader(open(find("kernel_trace.csv"))) if all_pat in r["Kernel_Name"]]
     r = json.loads([line for line in open(bench_log) if line.startswith("{")][-1])
     rf = r["roofline"]
-    first = r.get("clock_settle", {}).get("calls", 0) + r["warmup"]
+    graph = r.get("launch") == "hip_graph"
+    # settle calls, warm-up steps and, with --graph, the untimed replay
+    first = r.get("clock_settle", {}).get("calls", 0) + r["warmup"] + (r["steps"] if graph else 0)
     by = {}
     for t in trace:
         by.setdefault(t["Kernel_Name"], []).append(
@@ -410,7 +412,7 @@ def summarize_trace(trace_dir: str, bench_log: str, workload: str) -> str:
         parts.append(f"`{name[:70]}` {avg:.0f} ns over {len(timed)} dispatches")
     ev_ns = rf["kernel_ms"] * 1e6
     cmd = " ".join(a for a in ["python3 bench.py --workload", workload, "--steps", str(r["steps"]),
-                               "--cpu-budget 0"])
+                               "--cpu-budget 0"] + (["--graph"] if graph else []))
     lines = [
         f"# Kernel trace, workload {workload}",
         "",
@@ -436,7 +438,8 @@ def summarize_trace(trace_dir: str, bench_log: str, workload: str) -> str:
         "Timed region (dispatches " + f"{first} .. {first + r['steps'] - 1} of each kernel): "
         + "; ".join(parts) + ".",
         "",
-        f"Same run, HIP events on the launch stream around the {r['steps']} timed calls: {ev_ns:.0f} ns per call, "
+        f"Same run, HIP events on the launch stream around the {r['steps']} timed calls"
+        f"{' (one replay of a captured HIP graph)' if graph else ''}: {ev_ns:.0f} ns per call, "
         f"{r['value']} {r['unit']} ({100 * rf['frac']:.1f}% of {rf['peak']} {rf['unit']}); graphics clock "
         f"median {rf.get('gfx_clock_mhz_median')} MHz, socket power median "
         f"{rf.get('socket_power_w_median')} W (per-call window after the timed region).  Trace average "

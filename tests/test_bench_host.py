@@ -177,3 +177,29 @@ def test_counter_summary_reads_units_and_per_tile_counts(tmp_path, monkeypatch):
     assert "cycles per vector instruction (4 x SQ_ACTIVE_INST_VALU / SQ_INSTS_VALU): 4.00" in text
     assert "vector (not MFMA) 220.0, MFMA 80.0" in text
     assert "other_kernel" not in text
+
+
+def test_trace_summary_skips_the_untimed_graph_replay(tmp_path, monkeypatch):
+    """With --graph the timed replay follows one untimed replay of the same
+    `steps` dispatches, so the timed region starts `steps` dispatches later."""
+    import json
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    d = tmp_path / "trace" / "host"
+    d.mkdir(parents=True)
+    name = "_ZN2fa_fwd_f32_q4_kernel"
+    with open(d / "trace_kernel_stats.csv", "w") as f:
+        f.write('"Name","Calls","TotalDurationNs","AverageNs","Percentage","MinNs","MaxNs","StdDev"\n')
+        f.write(f'"{name}",25,0,150,100,100,300,10\n')
+    with open(d / "trace_kernel_trace.csv", "w") as f:
+        f.write("Kernel_Name,Start_Timestamp,End_Timestamp\n")
+        for i in range(25):  # 5 warm-up + 10 untimed replay at 100 ns, 10 timed at 200 ns
+            dur = 100 if i < 15 else 200
+            f.write(f"{name},{1000 * i},{1000 * i + dur}\n")
+    log = tmp_path / "bench.log"
+    rec = {"value": 1.0, "unit": "TFLOP/s", "steps": 10, "warmup": 5, "launch": "hip_graph",
+           "clock_settle": {"calls": 0},
+           "roofline": {"kernel_ms": 0.0002, "frac": 0.5, "peak": 2.0, "unit": "TFLOP/s"}}
+    log.write_text(json.dumps(rec) + "\n")
+    text = open(bench.summarize_trace(str(tmp_path / "trace"), str(log), "single_head_f32")).read()
+    assert "200 ns over 10 dispatches" in text
+    assert "--graph" in text and "captured HIP graph" in text
