@@ -157,7 +157,7 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Params p) {
   const int64_t wave_end = CAUSAL ? (qw + 32 < N ? qw + 32 : N) : N;
   const int wave_tiles = qw < N ? (int)((wave_end + BC - 1) / BC) : 0;
 
-  // ---- tile loads: global -> LDS, 16 bytes per lane (group B) --------------
+  // ---- tile loads: global -> LDS, 16 bytes per lane (K: group B, V: group A) 
   int kvoff[LPW], vvoff[LPW];
 #pragma unroll
   for (int j = 0; j < LPW; ++j) {
@@ -365,7 +365,13 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Params p) {
   barrier();
 
   // The same slot schedule as the 16-bit kernel: group A runs M(t) while group
-  // B runs V(t-1) and loads K(t+2), V(t+1); then they swap.
+  // B runs V(t-1), then they swap.  Loads as in the 16-bit kernel at d = 64:
+  // group B issues K(t+2) at the start of its V phase; group A issues V(t) at
+  // the end of its M(t) (its buffer's last reader, B's M(t-1), finished a slot
+  // earlier) and waits for it at the end of its V(t) phase, before V(t)'s first
+  // reader in slot 2t+2.  With the products at twice the 16-bit rate the
+  // softmax phase is the longer one, so A issues in time it would otherwise
+  // spend waiting at the barrier.
   auto iteration = [&](int t, auto mwork, auto vwork) {
     wave_priority<1>();
     mwork();
@@ -375,19 +381,17 @@ __global__ void __launch_bounds__(512, 1) fwd_fp8_kernel(Fp8Params p) {
     for (int db = 0; db < ND; ++db) fence(o[db]);
     fence(lsum);
     wave_priority<0>();
+    if (!group_b) issue_v(t);  // A: V(t) at the end of its M(t), in slot 2t
     if (group_b) wait_loads();
     barrier();
-    if (group_b) {
-      issue_k(t + 2);
-      issue_v(t + 1);
-    }
+    if (group_b) issue_k(t + 2);
     vwork();
+    if (!group_b) wait_loads();
     barrier();
   };
   const int W = wave_tiles;
   if (group_b) {
     issue_k(1);
-    issue_v(0);
     barrier();
   }
   iteration(
