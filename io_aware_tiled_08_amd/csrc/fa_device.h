@@ -50,6 +50,21 @@ __device__ __forceinline__ float halves_sum(float x) {
   return bits<float>(r[0]) + bits<float>(r[1]);
 }
 
+// max / sum over lanes l, l^16, l^32, l^48 (the four lane groups of a 16x16
+// MFMA result column): halves first, then v_permlane16_swap, which exchanges
+// the odd 16-lane rows of its first operand with the even rows of its second,
+// so with both operands x the results hold x of lanes l and l^16.
+__device__ __forceinline__ float quad_max(float x) {
+  x = halves_max(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(bits<uint32_t>(x), bits<uint32_t>(x), false, false);
+  return fmaxf(bits<float>(r[0]), bits<float>(r[1]));
+}
+__device__ __forceinline__ float quad_sum(float x) {
+  x = halves_sum(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(bits<uint32_t>(x), bits<uint32_t>(x), false, false);
+  return bits<float>(r[0]) + bits<float>(r[1]);
+}
+
 // In the 32x32 MFMA accumulator, register r of a lane in wave half hh holds
 // row 8*(r/4) + 4*hh + r%4.  The kernels feed K so that this row carries key
 //   key_of_reg(r, hh) = 16*(r/8) + 8*hh + r%8

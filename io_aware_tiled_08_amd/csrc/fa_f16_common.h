@@ -4,6 +4,8 @@
 // register fences and two forms of a maximum over many values.
 #pragma once
 
+#include <type_traits>
+
 #include "fa_device.h"
 
 namespace fa {
@@ -85,6 +87,36 @@ struct Swizzle {
     return D == 128 ? c ^ ((r & 3) << 2) : c ^ (((r >> 1) & 1) << 2);
   }
 };
+
+// Chunk swizzles for reads of 16x16x32 operands.  K: 16 lanes read one chunk
+// of rows 8*(m/4) + m%4 (m = 0..15, plus a block offset in row bits 2, 5 and
+// 6), so the 16 rows must land in 16 different bank groups (d = 128: 16-chunk
+// rows; d = 64: 8-chunk rows, two rows per bank period, so 8 per half).  V:
+// each 32-lane half of a transposing read covers 32 bytes (two chunks) of
+// rows 8*g + 0..3, g = 0, 1, so the 8 chunk pairs must not collide.
+template <int D>
+struct Swizzle16 {
+  static_assert(D == 64 || D == 128, "head dim");
+  static __device__ __forceinline__ constexpr int k(int r, int c) {
+    return D == 128 ? c ^ ((r & 3) | (((r >> 3) & 3) << 2))
+                    : c ^ (((r >> 1) & 1) | (((r >> 3) & 3) << 1));
+  }
+  static __device__ __forceinline__ constexpr int v(int r, int c) {
+    return D == 128 ? c ^ (2 * ((r & 3) | (((r >> 3) & 1) << 2)))
+                    : c ^ (2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1)));
+  }
+};
+
+// v_mfma_f32_16x16x32_{f16,bf16}: A lane l supplies row l%16 and k = 8*(l/16)
+// .. +7, B lane l column l%16 with the same k, and the four result registers
+// of lane l hold rows 4*(l/16) + r of column l%16.
+template <typename T>
+__device__ __forceinline__ f32x4 mma16(typename Half<T>::Frag a, typename Half<T>::Frag b, f32x4 c) {
+  if constexpr (std::is_same_v<T, __bf16>)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
 
 typedef short s16x4 __attribute__((vector_size(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;

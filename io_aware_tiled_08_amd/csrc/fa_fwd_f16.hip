@@ -23,7 +23,7 @@
 //     O += P(t-1) V(t-1) followed by S(t) = K(t) Q^T, and its V phase turns
 //     S(t) into P(t).  The softmax's vector instructions issue while the
 //     partner wave's matrix products run (a wave64 fp32 VALU op occupies the
-//     vector pipe 4 cycles, exp 8; a 32x32x16 MFMA the matrix pipe 32).  The
+//     vector pipe 4 cycles, exp 8; a 16x16x32 MFMA the matrix pipe 16).  The
 //     wave in its M phase runs at issue priority 1, its partner at 0.
 //   * K and V tiles (128 keys) are double buffered in LDS and filled by
 //     buffer_load ... lds (HBM/L2 straight into LDS, no register staging).
@@ -40,14 +40,21 @@
 //     stored XOR-permuted so that the operand reads hit all LDS banks; the
 //     permutation is applied on the global side (lane i of a load always
 //     writes LDS bytes 16i..16i+15).
-//   * S^T = K Q^T on v_mfma_f32_32x32x16_{f16,bf16}: a lane owns one query
-//     (accumulator column) and 16 keys of each 32-key block, the other 16 sit
-//     in lane l^32, so the row max is in-lane plus one v_permlane32_swap,
-//     and the rescale factor is a per-lane scalar.  Q stays in registers for
-//     the whole loop.
+//   * S^T = K Q^T on v_mfma_f32_16x16x32_{f16,bf16}: a wave's 32 queries are
+//     two 16-query blocks, the 128-key tile eight 16-key blocks, and each K
+//     fragment read from LDS feeds both query blocks.  A lane owns one query
+//     of each block (its result column) and 4 keys of each key block; the
+//     other 12 keys of a block sit in lanes l^16, l^32, l^48, so a row
+//     maximum or sum is in-lane plus two lane swaps.  On this card the 16x16
+//     products run about 20% cooler per FLOP than 32x32x16 (their accumulators
+//     are a quarter the size), and under the power limit that buys clock: the
+//     headline kernel ran 7-8% faster than the same pass on 32x32 tiles.
+//     Q stays in registers for the whole loop.
 //   * O^T += V^T P^T: P^T is the B operand taken straight from the score
-//     registers (rounded to the input type), V^T comes from row-major V in
-//     LDS through ds_read_b64_tr_b16 transposing loads.  The row sum of the
+//     registers (rounded to the input type): K rows are fed so that the 4
+//     keys a lane holds in key block 2j and the 4 it holds in block 2j+1 are
+//     8 consecutive keys of P V step j.  V^T comes from row-major V in LDS
+//     through ds_read_b64_tr_b16 transposing loads.  The row sum of the
 //     rounded weights is formed next to these products on the matrix pipe
 //     (4x4x4 products against an all-ones operand), not on the vector ALU.
 //   * exp is exp2 with log2(e) folded into the scale.  The reference maximum
@@ -85,16 +92,17 @@ __device__ __forceinline__ void fwd_f16_tiles(const KernelParams& p, const WorkI
   using H = Half<T>;
   using Frag = typename H::Frag;
   using Pair = typename H::Pair;
-  using Sw = Swizzle<D>;
+  using Sw = Swizzle16<D>;
   constexpr int NW = 8;              // waves per workgroup
   constexpr int BR = NW * 32;        // query rows per workgroup
   constexpr int BC = 128;            // keys per tile
   constexpr int RB = D * 2;          // bytes per row of K or V
   constexpr int CPR = D / 8;         // 16-byte chunks per row
   constexpr int TILE = BC * RB;      // bytes of one staged K (or V) tile
-  constexpr int NKB = BC / 32;       // 32-key blocks per tile
-  constexpr int NKS = D / 16;        // MFMAs per 32x32 score block
-  constexpr int ND = D / 32;         // 32-row blocks of O^T
+  constexpr int NKB = BC / 16;       // 16-key blocks of S^T per tile
+  constexpr int NKS = D / 32;        // 32-deep steps per score block
+  constexpr int NJ = BC / 32;        // 32-key steps of O^T += V^T P^T
+  constexpr int NDB = D / 16;        // 16-row blocks of O^T
   constexpr int RPL = 1024 / RB;     // rows one wave-wide 1 KiB load covers
   constexpr int LPW = TILE / 1024 / 4;  // 1 KiB loads per loading wave per tensor
   static_assert(LPW >= 1 && TILE % 4096 == 0, "tile shape");
@@ -107,11 +115,10 @@ __device__ __forceinline__ void fwd_f16_tiles(const KernelParams& p, const WorkI
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool group_b = wave >= 4;
   const int gw = wave & 3;  // wave index inside its group
-  const int l32 = lane & 31;
-  const int hh = lane >> 5;
+  const int l16 = lane & 15;  // query of the lane within a 16-query block
+  const int lg = lane >> 4;   // 16-lane group: keys 4*lg .. of a 16-key block, or 8*lg .. of a 32-key step
   const int64_t q0 = (int64_t)wi.qblk * BR;
   const int64_t qw = q0 + (int64_t)wave * 32;
-  const int64_t qrow = qw + l32;
 
   const T* __restrict__ Qh = (const T*)p.q + wi.bh * N * D;
   const T* __restrict__ Kh = (const T*)p.k + wi.bh * N * D;
@@ -233,136 +240,157 @@ __device__ __forceinline__ void fwd_f16_tiles(const KernelParams& p, const WorkI
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // Q (B operand of S^T = K Q^T): lane holds Q[qrow][16*ks + 8*hh .. +7].
+  // Q (B operand of S^T = K Q^T, one per 16-query block qb): lane holds
+  // Q[qw + 16*qb + l16][32*ks + 8*lg .. +7].
   // The stream loads each item's Q through a buffer resource that ends at row
   // N (rows past it read as zeros), so that nothing waits for the data before
   // the products that use it; only a negative scale (a sign flip of Q) reads
   // it at once.
-  Frag qf[NKS];
+  Frag qf[2][NKS];
   auto load_q = [&](const WorkItem w) {
     const int64_t q0 = (int64_t)w.qblk * BR;
     const int64_t rows = N - q0 < BR ? N - q0 : BR;
     const auto rs = __builtin_amdgcn_make_buffer_rsrc(
         (void*)((const T*)p.q + (w.bh * N + q0) * D), (short)0, (int)(rows * RB), 0x00020000);
-    const int off = (wave * 32 + l32) * RB + hh * 16;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks)
-      qf[ks] = bits<Frag>(__builtin_amdgcn_raw_buffer_load_b128(rs, off, 32 * ks, 0));
+    for (int qb = 0; qb < 2; ++qb) {
+      const int off = (wave * 32 + 16 * qb + l16) * RB + lg * 16;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        qf[qb][ks] = bits<Frag>(__builtin_amdgcn_raw_buffer_load_b128(rs, off, 64 * ks, 0));
+    }
     if (p.q_sign) {
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) qf[ks] = bits<Frag>(bits<u32x4>(qf[ks]) ^ p.q_sign);
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) qf[qb][ks] = bits<Frag>(bits<u32x4>(qf[qb][ks]) ^ p.q_sign);
     }
   };
   if constexpr (STREAM) {
     load_q(first);
   } else {
-    const bool ok = qrow < N;
-    const T* src = Qh + (ok ? qrow : 0) * D + hh * 8;
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      u32x4 raw = ok ? *(const u32x4*)(src + ks * 16) : u32x4{0, 0, 0, 0};
-      raw ^= p.q_sign;
-      qf[ks] = bits<Frag>(raw);
+    for (int qb = 0; qb < 2; ++qb) {
+      const int64_t qr = qw + 16 * qb + l16;
+      const bool ok = qr < N;
+      const T* src = Qh + (ok ? qr : 0) * D + lg * 8;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        u32x4 raw = ok ? *(const u32x4*)(src + ks * 32) : u32x4{0, 0, 0, 0};
+        raw ^= p.q_sign;
+        qf[qb][ks] = bits<Frag>(raw);
+      }
     }
   }
   if (group_b) issue_k(0);
 
   // ---- lane-constant LDS read offsets ----------------------------------------
-  // K A operand for MFMA ks of key block kb: row kb*32 + krow, chunk 2*ks + hh
-  // (the swizzle only sees the row modulo 16, so kb does not change it).
-  const int krow = k_row_of_lane(l32);
+  // K A operand for step ks of key block kb: the lane feeds row m = l16 of
+  // the block with key 32*(kb/2) + 8*(m/4) + 4*(kb%2) + m%4 of the tile, so
+  // that register r of lane group lg in the product holds key
+  // 32*(kb/2) + 8*lg + 4*(kb%2) + r: the 8 keys lane group lg contributes to
+  // one 32-deep P V step are 8 consecutive keys, 4 from block 2j and 4 from
+  // block 2j+1.  Chunk 4*ks + lg of the row; the swizzle ignores row bits 2, 5
+  // and 6, so the block only adds a constant.
+  const int krow = 8 * (l16 >> 2) + (l16 & 3);
   int koff[NKS];
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) koff[ks] = krow * RB + Sw::k(krow, 2 * ks + hh) * 16;
-  // V^T A operand for O^T block db, keys kb*32 + 16*jj + 8*hh + 4*t + 0..3:
-  // lane j of 16-lane group g addresses row (.. + j/4) at columns
-  // db*32 + 16*(g%2) + 4*(j%4); the swizzle only sees the row modulo 4.
-  int voff[ND];
+  for (int ks = 0; ks < NKS; ++ks) koff[ks] = krow * RB + Sw::k(krow, 4 * ks + lg) * 16;
+  // V^T A operand for O^T block db, keys 32*j + 8*lg + 0..7: lane j16 of
+  // group lg addresses row 32*j + 8*lg + j16/4 (+4 for the second half) at
+  // columns 16*db + 4*(j16%4); the swizzle ignores row bits 2, 5 and 6.
+  int voff[NDB];
   {
-    const int g = lane >> 4, j16 = lane & 15;
-    const int vrow = 8 * hh + (j16 >> 2);
+    const int vrow = 8 * lg + (l16 >> 2);
 #pragma unroll
-    for (int db = 0; db < ND; ++db) {
-      const int dcol = db * 32 + 16 * (g & 1) + 4 * (j16 & 3);
+    for (int db = 0; db < NDB; ++db) {
+      const int dcol = db * 16 + 4 * (l16 & 3);
       voff[db] = vrow * RB + Sw::v(vrow, dcol >> 3) * 16 + (dcol & 7) * 2;
     }
   }
 
   // ---- running state ----------------------------------------------------------
-  f32x16 o[ND];
+  f32x4 o[NDB][2];
 #pragma unroll
-  for (int db = 0; db < ND; ++db) o[db] = f32x16{};
-  f32x16 s[NKB];
-  Frag pf[NKB][2];
-  float m = kNegInf;  // reference maximum of the row, log2 units
-  // This lane's share of the row sum (the keys it holds), accumulated on the
+  for (int db = 0; db < NDB; ++db) o[db][0] = o[db][1] = f32x4{};
+  f32x4 s[NKB][2];
+  Frag pf[NJ][2];
+  float m[2] = {kNegInf, kNegInf};  // reference maximum of each of the lane's rows, log2 units
+  // This lane's share of each row sum (the keys it holds), accumulated on the
   // matrix pipe next to the P V products of the same weights; element 0 is
   // used (the product writes the same value to all four).
-  f32x4 lacc = f32x4{};
+  f32x4 lacc[2] = {f32x4{}, f32x4{}};
   const float c = p.c;
 
   // Epilogue of the stream's item w: O = O_acc / l, written once; LSE =
   // (m + log2 l) * ln 2.
   auto store = [&](const WorkItem w) {
-    const int64_t qrow = (int64_t)w.qblk * BR + (int64_t)wave * 32 + l32;
-    const float lt = halves_sum(lacc[0]);
-    if (qrow < N) {
-      const float inv = 1.0f / lt;
-      if (hh == 0) p.lse[w.bh * N + qrow] = (m + __builtin_amdgcn_logf(lt)) * kLn2;
-      T* dst = (T*)p.o + (w.bh * N + qrow) * D + hh * 4;
 #pragma unroll
-      for (int db = 0; db < ND; ++db)
+    for (int qb = 0; qb < 2; ++qb) {
+      const int64_t qrow = (int64_t)w.qblk * BR + (int64_t)wave * 32 + 16 * qb + l16;
+      const float lt = quad_sum(lacc[qb][0]);
+      if (qrow < N) {
+        const float inv = 1.0f / lt;
+        if (lg == 0) p.lse[w.bh * N + qrow] = (m[qb] + __builtin_amdgcn_logf(lt)) * kLn2;
+        T* dst = (T*)p.o + (w.bh * N + qrow) * D + lg * 4;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const Pair lo = H::pack(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
-          const Pair hi = H::pack(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
-          *(u32x2*)(dst + db * 32 + g * 8) = u32x2{bits<uint32_t>(lo), bits<uint32_t>(hi)};
+        for (int db = 0; db < NDB; ++db) {
+          const Pair lo = H::pack(o[db][qb][0] * inv, o[db][qb][1] * inv);
+          const Pair hi = H::pack(o[db][qb][2] * inv, o[db][qb][3] * inv);
+          *(u32x2*)(dst + db * 16) = u32x2{bits<uint32_t>(lo), bits<uint32_t>(hi)};
         }
+      }
     }
   };
 
   // M phase of tile t: O += P(t-1) V(t-1), then S(t) = K(t) Q^T: NPV + NS
-  // matrix products whose A operands come from LDS.  In the steady state
-  // (m_pv_s) the operand reads run kPipe products ahead of the products, so
+  // A fragments from LDS, each feeding the two 16-query blocks' products.  In
+  // the steady state (m_pv_s) the fragment reads run kPipe fragments ahead of
+  // the products, so
   // LDS latency hides under the matrix pipe; the sched_group_barrier pairs
   // pin that order.  A wave's first tile has no P V product and its last
   // (t = wave_tiles, or g = total in the stream) no score product (m_s,
   // m_pv).
-  constexpr int NPV = NKB * 2 * ND;  // O^T += V^T P^T products
-  constexpr int NS = NKS * NKB;      // S^T = K Q^T products
+  constexpr int NPV = NJ * NDB;   // V^T fragments (each feeds both 16-query blocks)
+  constexpr int NS = NKS * NKB;   // K fragments (each feeds both 16-query blocks)
   constexpr int kPipe = 3;
   auto fetch = [&](const char* vl, const char* kl, int i) -> Frag {
     if (i < NPV) {
-      const int kb = i / (2 * ND), jj = (i / ND) % 2, db = i % ND;
-      const int off = (kb * 32 + 16 * jj) * RB + voff[db];
+      const int j = i / NDB, db = i % NDB;
+      const int off = 32 * j * RB + voff[db];
       const u32x2 lo = lds_read_tr(vl, off);
       const u32x2 hi = lds_read_tr(vl, off + 4 * RB);
       return bits<Frag>(u32x4{lo[0], lo[1], hi[0], hi[1]});
     }
-    const int j = i - NPV, ks = j / NKB, kb = j % NKB;
-    return bits<Frag>(*(const u32x4*)(kl + kb * 32 * RB + koff[ks]));
+    const int jj = i - NPV, ks = jj / NKB, kb = jj % NKB;
+    return bits<Frag>(*(const u32x4*)(kl + (32 * (kb >> 1) + 4 * (kb & 1)) * RB + koff[ks]));
   };
   auto apply = [&](int i, Frag a) {
     if (i < NPV) {
-      const int kb = i / (2 * ND), jj = (i / ND) % 2, db = i % ND;
-      o[db] = H::mma(a, pf[kb][jj], o[db]);
-      if (db == ND - 1) {
-        const u32x4 w = bits<u32x4>(pf[kb][jj]);
-        lacc = H::sum4(u32x2{w[0], w[1]}, lacc);
-        lacc = H::sum4(u32x2{w[2], w[3]}, lacc);
+      const int j = i / NDB, db = i % NDB;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) o[db][qb] = mma16<T>(a, pf[j][qb], o[db][qb]);
+      if (db == NDB - 1) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          const u32x4 w = bits<u32x4>(pf[j][qb]);
+          lacc[qb] = H::sum4(u32x2{w[0], w[1]}, lacc[qb]);
+          lacc[qb] = H::sum4(u32x2{w[2], w[3]}, lacc[qb]);
+        }
       }
     } else {
-      const int j = i - NPV, ks = j / NKB, kb = j % NKB;
-      s[kb] = H::mma(a, qf[ks], s[kb]);
+      const int jj = i - NPV, ks = jj / NKB, kb = jj % NKB;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) s[kb][qb] = mma16<T>(a, qf[qb][ks], s[kb][qb]);
     }
   };
   auto m_pv_s = [&](int t) {
     const char* vl = &smem[1][(t - 1) & 1][0];
     const char* kl = &smem[0][t & 1][0];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+    for (int kb = 0; kb < NKB; ++kb) s[kb][0] = s[kb][1] = f32x4{};
     Frag ring[kPipe];
-    constexpr int PRE = 2 * kPipe;  // the first kPipe products are P V products
+    constexpr int PRE = 2 * kPipe;  // the first kPipe fragments are V^T fragments
     static_assert(kPipe <= NPV, "pipeline prologue");
 #pragma unroll
     for (int i = 0; i < kPipe; ++i) ring[i] = fetch(vl, kl, i);
@@ -379,10 +407,10 @@ __device__ __forceinline__ void fwd_f16_tiles(const KernelParams& p, const WorkI
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
       }
-      if (i < NPV && i % ND == ND - 1) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);  // with the two row-sum products
+      if (i < NPV && i % NDB == NDB - 1) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);  // with the four row-sum products
       } else {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       }
     }
   };
@@ -394,7 +422,7 @@ __device__ __forceinline__ void fwd_f16_tiles(const KernelParams& p, const WorkI
   auto m_s = [&](int t) {
     const char* kl = &smem[0][t & 1][0];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) s[kb] = f32x16{};
+    for (int kb = 0; kb < NKB; ++kb) s[kb][0] = s[kb][1] = f32x4{};
 #pragma unroll
     for (int i = NPV; i < NPV + NS; ++i) apply(i, fetch(kl, kl, i));
   };
@@ -413,69 +441,79 @@ __device__ __forceinline__ void fwd_f16_tiles(const KernelParams& p, const WorkI
       if (t == 0 && sc.g > 0) {
         store(done);
 #pragma unroll
-        for (int db = 0; db < ND; ++db) o[db] = f32x16{};
-        lacc = f32x4{};
-        m = kNegInf;
+        for (int db = 0; db < NDB; ++db) o[db][0] = o[db][1] = f32x4{};
+        lacc[0] = lacc[1] = f32x4{};
+        m[0] = m[1] = kNegInf;
       }
     }
     const int64_t k0 = (int64_t)t * BC;
     // Keys k0 + i with i >= lim are invisible (past N, or after the query
-    // when causal): their scores become -inf.  Register r of key block kb
-    // holds key kb*32 + key_of_reg(r, hh) of the tile.
-    int64_t lim64 = N - k0;
-    if (CAUSAL && qrow + 1 - k0 < lim64) lim64 = qrow + 1 - k0;
+    // when causal): their scores become -inf.  Register r of block kb, lane
+    // group lg, holds key 32*(kb/2) + 8*lg + 4*(kb%2) + r of the tile.
     const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > qw);
     if (need_mask) {
-      const int lim = (int)(lim64 < 0 ? 0 : (lim64 > BC ? BC : lim64)) - 8 * hh;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+      for (int qb = 0; qb < 2; ++qb) {
+        const int64_t qr = qw + 16 * qb + l16;
+        int64_t lim64 = N - k0;
+        if (CAUSAL && qr + 1 - k0 < lim64) lim64 = qr + 1 - k0;
+        const int lim = (int)(lim64 < 0 ? 0 : (lim64 > BC ? BC : lim64)) - 8 * lg;
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (kb * 32 + key_of_reg(r, 0) >= lim) s[kb][r] = kNegInf;
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (32 * (kb >> 1) + 4 * (kb & 1) + r >= lim) s[kb][qb][r] = kNegInf;
+      }
     }
-    // Row maximum as a tree (short dependency chains), then across halves.
-    float mx = chain_max4<NKB * 16>([&](int i) { return s[i / 16][i % 16]; });
-    mx = halves_max(mx);
-    const float mxc = mx * c;  // c > 0, so -inf stays -inf
-
-    // Online softmax: raise the reference maximum (and rescale l and O by
-    // exp2(m_old - m_new)) only when this tile exceeds it by the slack.
-    // m = -inf means no visible key yet: any visible key raises it.
-    const bool grow = mxc > m + kRescaleSlack;
-    if (__ballot(grow)) {
-      const float alpha = grow ? __builtin_amdgcn_exp2f(m - mxc) : 1.0f;
-      m = grow ? mxc : m;
-      lacc *= alpha;
+    // Online softmax per row (two rows per lane, one per query block): raise
+    // the reference maximum only when this tile exceeds it by the slack.
+    float mxc[2];
+    bool grow[2];
 #pragma unroll
-      for (int db = 0; db < ND; ++db) o[db] *= alpha;
+    for (int qb = 0; qb < 2; ++qb) {
+      float mx = chain_max4<NKB * 4>([&](int i) { return s[i / 4][qb][i % 4]; });
+      mx = quad_max(mx);
+      mxc[qb] = mx * c;  // c > 0, so -inf stays -inf
+      grow[qb] = mxc[qb] > m[qb] + kRescaleSlack;
     }
-    // A lane whose row has seen no visible key yet keeps m = -inf; its
-    // weights are exp2(-inf) = 0 either way.
-    const float m_use = m == kNegInf ? 0.f : m;
-
-    // P = exp2(c*s - m), rounded to T (the row sum is formed from these
-    // rounded weights in the next matrix phase, so O's normalisation matches
-    // the weights P V actually uses).  Masked scores are -inf and c > 0, so
-    // their weight is exp2(-inf) = 0.
+    if (__ballot(grow[0] || grow[1])) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+      for (int qb = 0; qb < 2; ++qb) {
+        const float alpha = grow[qb] ? __builtin_amdgcn_exp2f(m[qb] - mxc[qb]) : 1.0f;
+        m[qb] = grow[qb] ? mxc[qb] : m[qb];
+        lacc[qb] *= alpha;
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
+        for (int db = 0; db < NDB; ++db) o[db][qb] *= alpha;
+      }
+    }
+    // P = exp2(c*s - m), rounded to T; P V step j takes keys 8*lg .. +7 of
+    // its 32 from blocks 2j (registers 0..3) and 2j+1 (registers 0..3).
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const float m_use = m[qb] == kNegInf ? 0.f : m[qb];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
         u32x4 f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * jj + 2 * i], c, -m_use));
-          const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * jj + 2 * i + 1], c, -m_use));
-          f[i] = bits<uint32_t>(H::pack(e0, e1));
-        }
-        pf[kb][jj] = bits<Frag>(f);
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * j + h][qb][2 * e], c, -m_use));
+            const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * j + h][qb][2 * e + 1], c, -m_use));
+            f[2 * h + e] = bits<uint32_t>(H::pack(e0, e1));
+          }
+        pf[j][qb] = bits<Frag>(f);
       }
+    }
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) fence(pf[kb][jj]);
-    fence(lacc);
-    fence(m);
+    for (int j = 0; j < NJ; ++j) {
+      fence(pf[j][0]);
+      fence(pf[j][1]);
+    }
+    fence(lacc[0]);
+    fence(lacc[1]);
+    fence(m[0]);
+    fence(m[1]);
     if constexpr (STREAM) {
       if (t == n_tiles - 1) {
         done = sc.w;
@@ -508,10 +546,17 @@ __device__ __forceinline__ void fwd_f16_tiles(const KernelParams& p, const WorkI
     wave_priority<1>();
     mwork();
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) fence(s[kb]);
+    for (int kb = 0; kb < NKB; ++kb) {
+      fence(s[kb][0]);
+      fence(s[kb][1]);
+    }
 #pragma unroll
-    for (int db = 0; db < ND; ++db) fence(o[db]);
-    fence(lacc);
+    for (int db = 0; db < NDB; ++db) {
+      fence(o[db][0]);
+      fence(o[db][1]);
+    }
+    fence(lacc[0]);
+    fence(lacc[1]);
     wave_priority<0>();
     if (kEarlyV && !group_b) issue_v(t);
     if (group_b) wait_loads();
@@ -545,21 +590,9 @@ __device__ __forceinline__ void fwd_f16_tiles(const KernelParams& p, const WorkI
   if (!group_b) barrier();
 
   // ---- epilogue: O = O_acc / l, written once; LSE = (m + log2 l) * ln 2 ----
-  const float lt = halves_sum(lacc[0]);
-  if (qrow < N) {
-    const float inv = 1.0f / lt;
-    if (hh == 0) Lh[qrow] = (m + __builtin_amdgcn_logf(lt)) * kLn2;
-    T* dst = Oh + qrow * D + hh * 4;
-#pragma unroll
-    for (int db = 0; db < ND; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const Pair lo = H::pack(o[db][4 * g] * inv, o[db][4 * g + 1] * inv);
-        const Pair hi = H::pack(o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
-        *(u32x2*)(dst + db * 32 + g * 8) = u32x2{bits<uint32_t>(lo), bits<uint32_t>(hi)};
-      }
-  }
+  store(wi);
 }
+
 
 // One workgroup per 256-row block; the hardware dispatcher hands the blocks
 // to CUs in the order of work_item (longest first when causal).
