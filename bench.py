@@ -548,8 +548,10 @@ class ClockSampler:
 def calibrate(seconds: float = 1.5) -> None:
     """Reachable fp16 matrix throughput on this card, with the clock and socket
     power held under it: hipBLASLt square GEMMs (torch.matmul, n = 8192 and
-    16384) and a register-only chain of 32x32x16 f16 MFMAs (libfa_calib.so,
-    256 workgroups x 8 waves x 4 chains).  Prints one JSON line per case.  The
+    16384) and register-only chains of f16 MFMAs (libfa_calib.so, 256
+    workgroups x 8 waves, 131072 FLOPs per wave and step) for the 32x32x16 and
+    16x16x32 shapes, each with small and with unit-variance operands.  Prints
+    one JSON line per case.  The
     attention kernel's roofline fraction is quoted against the published dense
     peak; these lines say how much of that peak the card sustains at all
     under its power limit."""
@@ -597,15 +599,17 @@ def calibrate(seconds: float = 1.5) -> None:
         measure(f"gemm_f16_n{n}", lambda: torch.matmul(a, b, out=c), reps, 2.0 * n ** 3)
         del a, b, c
     lib = ctypes.CDLL(CALIB_LIB_PATH)
-    lib.fa_calib_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.fa_calib_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_void_p]
     blocks, iters = 256, 20000
     out = torch.empty(blocks * 512, device=dev)
-
-    def chain():
-        rc = lib.fa_calib_mfma(out.data_ptr(), blocks, iters, stream.cuda_stream)
-        if rc != 0:
-            raise RuntimeError(f"fa_calib_mfma failed ({rc})")
-    measure("mfma_chain_f16_32x32x16", chain, 20, float(blocks) * 8 * 4 * iters * 32768)
+    for shape, label in enumerate(("32x32x16", "16x16x32", "32x32x16_unitvar",
+                                   "16x16x32_unitvar")):
+        def chain(shape=shape):
+            rc = lib.fa_calib_mfma(out.data_ptr(), blocks, iters, shape, stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"fa_calib_mfma failed ({rc})")
+        measure(f"mfma_chain_f16_{label}", chain, 20, float(blocks) * 8 * iters * 131072)
 
 
 def cpu_baseline_cache(w, q, k, v, budget_s: float):
