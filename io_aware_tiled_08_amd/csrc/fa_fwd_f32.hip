@@ -225,32 +225,43 @@ __global__ void __launch_bounds__(F32Lds<D>::kWaves * 64, 1) fwd_f32_kernel(Kern
 // ---------------------------------------------------------------------------
 // Small fp32 problems at d = 64 (few 32-row blocks, e.g. one head of 512
 // queries): a workgroup owns only 4 query rows, so the launch spreads over
-// eight times as many CUs, and its 4 waves take every 4th chunk of 64 keys.
+// eight times as many CUs, and its 4 waves take every 4th chunk of 32 keys.
 //
 // v_mfma_f32_4x4x1_16b_f32 computes 16 independent 4x4 blocks; lane 4b + i
 // supplies row i of block b's A column, lane 4b + j column j of its B row,
-// and register r of lane 4b + j receives D[b][r][j].
-//   Scores:  block b = keys 4b .. 4b+3 of the chunk, columns = the 4 queries.
-//            Lane l supplies its own key row K[k0 + l][c] as A and its query's
-//            row Q[q0 + l%4][c] as B; after the D products over c, register r
-//            of lane 4b + j holds the score of key 4b + r against query j.
-//   P V:     product (r, c) takes block b's key 4b + r: B is register r of
-//            the weights (the lane's own query j), A in lane 4b + i is
-//            V[k0 + 4b + r][16 i + c].  Register i of lane 4b + j then sums
-//            V[.][16 i + c] P[j][.] over block b's keys: a partial O for query
-//            j, summed over the 16 blocks (and the waves) at the end.
+// and register r of lane 4b + j receives D[b][r][j].  Block b = 8h + bb:
+// the two halves h of the wave work on the same 32 keys (bb = key block).
+//   Scores:  lane (h, bb, i) supplies K[k0 + 4bb + i][32h + t] as A and
+//            lane (h, bb, j) Q[q0 + j][32h + t] as B at step t < 32; register
+//            r of lane (h, bb, j) then holds half h's share of the score of
+//            key 4bb + r against query j, and one lane swap between the
+//            halves adds the other share, so both halves hold the scores.
+//   P V:     product (r, c), c < 8: B is register r of the weights (the
+//            lane's own query j), A in lane (h, bb, i) is
+//            V[k0 + 4bb + r][16 i + 8h + c].  Register i of lane (h, bb, j)
+//            then sums V[.][16 i + 8h + c] P[j][.] over block bb's keys: a
+//            partial O for query j, summed over the 8 blocks (and the waves)
+//            at the end.
 // The online softmax is the 32-row kernel's: running max (in log2 units)
-// over the chunk, reduced across the 16 lanes of a query, rescale by
+// over the chunk, reduced across the lanes of a query, rescale by
 // exp2(m_old - m_new); each lane keeps a partial sum of its own weights.
-// Each wave sums its lanes' partial O over the 16 blocks (cross-lane), and
-// the waves' (O, m, l) are merged through LDS with weights 2^(m_w - M).
+//
+// Every workgroup streams its head's whole K and V through its CU, so the
+// CU's load path (about 64 bytes a cycle) and the loads' latency set the
+// time, not the products.  Chunks of 32 keys let each wave keep two of them
+// in flight in LDS (16 KiB each), so that path has work from the start:
+// each wave issues its first two chunks at once and chunk i+2 as soon as
+// chunk i is in registers.  Q is staged once per workgroup (one 1 KiB load).
+// At the end each wave's partial O (per lane and block) goes to LDS, and
+// every thread sums one output over the 8 blocks and the 4 waves with
+// weights 2^(m_w - M).
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kQ4Rows = 4;
-constexpr int kQ4Keys = 64;
+constexpr int kQ4Keys = 32;
 constexpr int kQ4Waves = 4;
 
-// Maximum or sum over the 16 lanes of one query (lanes congruent mod 4):
-// row rotations by 4 and 8 within each 16-lane row, then the row pairs
+// Maximum over the 16 lanes of one query (lanes congruent mod 4): row
+// rotations by 4 and 8 within each 16-lane row, then the row pairs
 // (permlane16 swap) and the halves (permlane32 swap).
 template <typename Op>
 __device__ __forceinline__ float query_reduce(float x, Op op) {
@@ -262,24 +273,32 @@ __device__ __forceinline__ float query_reduce(float x, Op op) {
   return op(bits<float>(r32[0]), bits<float>(r32[1]));
 }
 
+// s_waitcnt immediate for vmcnt(n) alone (gfx9 layout: vmcnt in bits 3:0 and
+// 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima), n <= 63.
+constexpr int vmcnt_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | 0x0F70; }
+
 template <bool CAUSAL>
 __global__ void __launch_bounds__(kQ4Waves * 64, 1) fwd_f32_q4_kernel(KernelParams p) {
   constexpr int D = 64;
   constexpr int RB = D * 4;              // bytes per K or V row
   constexpr int CH = kQ4Keys * RB;       // bytes of one chunk of K (or V)
-  // Each wave stages its chunk of K and of V in its own LDS area; after the
-  // loop the same LDS holds the waves' partial O for the merge.
-  __shared__ __attribute__((aligned(1024))) char smem[kQ4Waves][2][CH];
-  static_assert(sizeof(float) * kQ4Waves * 64 * 16 * 4 <= sizeof(smem), "merge area");
-  float(*part)[64][16][4] = (float(*)[64][16][4])&smem[0][0][0];  // [wave][lane][c][i]
-  __shared__ float m_lds[kQ4Waves][kQ4Rows], l_lds[kQ4Waves][kQ4Rows];
+  constexpr int PIECES = CH / 1024;      // 1 KiB loads per chunk of K (or V)
+  // [wave][buffer][K, V]; after the loop the same LDS holds the waves'
+  // partial O for the merge ([wave][lane][32 floats]).
+  __shared__ __attribute__((aligned(1024))) char smem[kQ4Waves][2][2][CH];
+  static_assert(sizeof(float) * kQ4Waves * 64 * 32 <= sizeof(smem), "merge area");
+  float(*part)[64][32] = (float(*)[64][32])&smem[0][0][0][0];
+  __shared__ __attribute__((aligned(16))) float q_lds[kQ4Rows][D];
+  __shared__ float m_lds[kQ4Waves][kQ4Rows];
+  __shared__ float l_lds[kQ4Waves][64];
 
   const int64_t N = p.N;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int j = lane & 3;   // query of the lane (B column / output column) and A row
-  const int b = lane >> 2;  // MFMA block
+  const int j = lane & 3;          // query of the lane (B column / output column) and A row
+  const int bb = (lane >> 2) & 7;  // key block
+  const int h = lane >> 5;         // half: d range 32h .. (scores), O columns 16 i + 8h .. (P V)
   const int64_t bh = blockIdx.x / p.n_qblk;
   int qblk = (int)(blockIdx.x % p.n_qblk);
   if (CAUSAL) qblk = p.n_qblk - 1 - qblk;  // longest blocks first
@@ -292,98 +311,116 @@ __global__ void __launch_bounds__(kQ4Waves * 64, 1) fwd_f32_q4_kernel(KernelPara
 
   const int64_t kv_end = CAUSAL ? (q0 + kQ4Rows < N ? q0 + kQ4Rows : N) : N;
   const int n_chunks = (int)((kv_end + kQ4Keys - 1) / kQ4Keys);
+  // This wave's chunks: wave, wave + 4, ...
+  const int n_mine = wave < n_chunks ? (n_chunks - wave + kQ4Waves - 1) / kQ4Waves : 0;
   const float c = p.c;
 
-  // Rows at or past N read as zeros (the buffer resources end there).
-  auto rows_rsrc = [&](const float* head, int64_t r0) {
-    const int64_t rows = N - r0 < 0 ? 0 : N - r0;
-    return __builtin_amdgcn_make_buffer_rsrc((void*)(head + r0 * D), (short)0,
-                                             (int)(rows * D * 4), 0x00020000);
-  };
-  auto load16 = [](float* dst, __amdgpu_buffer_rsrc_t rs, int off, uint32_t flip) {
-    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0) ^ flip;
-    dst[0] = bits<float>(x[0]);
-    dst[1] = bits<float>(x[1]);
-    dst[2] = bits<float>(x[2]);
-    dst[3] = bits<float>(x[3]);
-  };
-  // Chunk ch goes to this wave's LDS area by direct-to-LDS loads, read
+  // Chunk i of this wave goes to its buffer i % 2 by direct-to-LDS loads, read
   // coalesced (piece pc covers rows 4 pc .. 4 pc + 3; lane i fills LDS chunk
   // slot i % 16 of row 4 pc + i / 16).  Each row's 16-byte chunks are stored
-  // permuted so the operand reads below hit every bank group: chunk s of K row
-  // r at slot s ^ (r & 15) (lane l reads row l), chunk s of V row r at slot
-  // s ^ ((r >> 2) & 3) (16 lanes read rows 4b + r for four b, chunks 4i + k for
-  // four i).  The permutation is applied on the global side.
-  const uint32_t lds_k = lds_addr(&smem[wave][0][0]);
-  const uint32_t lds_v = lds_addr(&smem[wave][1][0]);
+  // permuted so the operand reads below spread evenly over the banks (four
+  // lanes per 16-byte bank group, the least 64 lanes of 16 bytes allow):
+  // chunk s of K row r at slot s ^ (r & 15), chunk s of V row r at slot
+  // s ^ ((r >> 2) & 3).  The permutation is applied on the global side; rows
+  // past N read as zeros (the buffer resources end there).
   const int prow = lane >> 4, slot = lane & 15;  // row within a piece, LDS slot
-  auto issue_chunk = [&](int ch) {
-    const int64_t k0 = (int64_t)ch * kQ4Keys;
+  auto issue = [&](int i) {
+    const int64_t k0 = (int64_t)(wave + kQ4Waves * i) * kQ4Keys;
     const int64_t rows = N - k0 < kQ4Keys ? N - k0 : kQ4Keys;
     const u32x4 rk = buffer_rsrc(Kh + k0 * D, (uint32_t)(rows * RB));
     const u32x4 rv = buffer_rsrc(Vh + k0 * D, (uint32_t)(rows * RB));
-    // Nothing may still read this area when the pieces start landing.
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    const uint32_t lk = lds_addr(&smem[wave][i & 1][0][0]);
+    const uint32_t lv = lds_addr(&smem[wave][i & 1][1][0]);
 #pragma unroll
-    for (int pc = 0; pc < CH / 1024; ++pc) {
+    for (int pc = 0; pc < PIECES; ++pc) {
       const int r = 4 * pc + prow;
-      dma_load16(rk, lds_k + pc * 1024, r * RB + (slot ^ (r & 15)) * 16);
-      dma_load16(rv, lds_v + pc * 1024, r * RB + (slot ^ ((r >> 2) & 3)) * 16);
+      dma_load16(rk, lk + pc * 1024, r * RB + (slot ^ (r & 15)) * 16);
+      dma_load16(rv, lv + pc * 1024, r * RB + (slot ^ ((r >> 2) & 3)) * 16);
     }
   };
-  // This lane's K row (key 64 ch + lane, all D values) and the V values it
-  // feeds as A operand (rows 4b .. 4b+3, columns 16 j .. 16 j + 15).
-  auto read_chunk = [&](float* kf, float* vf) {
-    const char* kl = &smem[wave][0][0];
-    const char* vl = &smem[wave][1][0];
+  // The lane's operands of chunk i: K row 4bb + j, d = 32h .. 32h + 31 (the
+  // A row index of the score product is the lane's j), and V rows 4bb + r,
+  // columns 16 i' + 8h .. +7 for i' = j (the A row index of the P V product).
+  auto read_chunk = [&](int i, float* kf, float* vf) {
+    const char* kl = &smem[wave][i & 1][0][0];
+    const char* vl = &smem[wave][i & 1][1][0];
+    const int kr = 4 * bb + j;
 #pragma unroll
-    for (int sc = 0; sc < D / 4; ++sc) {
-      const float4 x = *(const float4*)(kl + lane * RB + (sc ^ (lane & 15)) * 16);
-      kf[4 * sc] = x.x;
-      kf[4 * sc + 1] = x.y;
-      kf[4 * sc + 2] = x.z;
-      kf[4 * sc + 3] = x.w;
+    for (int s = 0; s < 8; ++s) {
+      const float4 x = *(const float4*)(kl + kr * RB + ((8 * h + s) ^ (kr & 15)) * 16);
+      kf[4 * s] = x.x;
+      kf[4 * s + 1] = x.y;
+      kf[4 * s + 2] = x.z;
+      kf[4 * s + 3] = x.w;
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int row = 4 * b + r;
-        const float4 x = *(const float4*)(vl + row * RB + ((4 * j + k) ^ (b & 3)) * 16);
-        vf[16 * r + 4 * k] = x.x;
-        vf[16 * r + 4 * k + 1] = x.y;
-        vf[16 * r + 4 * k + 2] = x.z;
-        vf[16 * r + 4 * k + 3] = x.w;
+      for (int k = 0; k < 2; ++k) {
+        const int row = 4 * bb + r;
+        const float4 x = *(const float4*)(vl + row * RB + ((4 * j + 2 * h + k) ^ ((row >> 2) & 3)) * 16);
+        vf[8 * r + 4 * k] = x.x;
+        vf[8 * r + 4 * k + 1] = x.y;
+        vf[8 * r + 4 * k + 2] = x.z;
+        vf[8 * r + 4 * k + 3] = x.w;
       }
   };
 
-  f32x4 acc[16];
+  // Q: one 1 KiB load by wave 0 into LDS (lane i: row i / 16, 16 bytes at
+  // chunk i % 16), issued before the chunks; rows past N read as zeros.
+  if (wave == 0) {
+    const int64_t rows = N - q0 < kQ4Rows ? N - q0 : kQ4Rows;
+    const u32x4 rq = buffer_rsrc(Qh + q0 * D, (uint32_t)(rows * RB));
+    dma_load16(rq, lds_addr(&q_lds[0][0]), lane * 16);
+  }
+  if (n_mine > 0) issue(0);
+  if (n_mine > 1) issue(1);
+  // Q, issued first, has landed when at most the chunk loads issued after it
+  // are outstanding (vmcnt counts a wave's loads in order).
+  if (wave == 0) {
+    if (n_mine > 1)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * PIECES));
+    else if (n_mine > 0)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PIECES));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  }
+  __syncthreads();
+  float qf[32];
 #pragma unroll
-  for (int cc = 0; cc < 16; ++cc) acc[cc] = f32x4{};
-  float m = kNegInf, lpart = 0.f;
-
-  // The first chunk's loads go out before Q's, so the two latencies overlap.
-  if (wave < n_chunks) issue_chunk(wave);
-  float qf[D];
-  {
-    const auto rs = rows_rsrc(Qh, q0);
-#pragma unroll
-    for (int i = 0; i < D / 4; ++i) load16(qf + 4 * i, rs, (j * D + 4 * i) * 4, p.q_sign);
+  for (int s = 0; s < 8; ++s) {
+    const u32x4 x = *(const u32x4*)&q_lds[j][32 * h + 4 * s] ^ p.q_sign;
+    qf[4 * s] = bits<float>(x[0]);
+    qf[4 * s + 1] = bits<float>(x[1]);
+    qf[4 * s + 2] = bits<float>(x[2]);
+    qf[4 * s + 3] = bits<float>(x[3]);
   }
 
-  auto compute = [&](const float* kf, const float* vf, int ch) {
-    const int64_t k0 = (int64_t)ch * kQ4Keys;
-    // Four independent accumulators (d mod 4), summed at the end.
+  f32x4 acc[8];
+#pragma unroll
+  for (int cc = 0; cc < 8; ++cc) acc[cc] = f32x4{};
+  float m = kNegInf, lpart = 0.f;
+
+  auto compute = [&](const float* kf, const float* vf, int i) {
+    const int64_t k0 = (int64_t)(wave + kQ4Waves * i) * kQ4Keys;
+    // Four independent accumulators (t mod 4), summed at the end; then the
+    // other half's share.
     f32x4 sp[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};
 #pragma unroll
-    for (int cc = 0; cc < D; ++cc) sp[cc & 3] = __builtin_amdgcn_mfma_f32_4x4x1f32(kf[cc], qf[cc], sp[cc & 3], 0, 0, 0);
+    for (int t = 0; t < 32; ++t)
+      sp[t & 3] = __builtin_amdgcn_mfma_f32_4x4x1f32(kf[t], qf[t], sp[t & 3], 0, 0, 0);
     f32x4 s = (sp[0] + sp[1]) + (sp[2] + sp[3]);
-    // Key 4b + r of the chunk against query qj; past N or after the query
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const auto x = __builtin_amdgcn_permlane32_swap(bits<uint32_t>(s[r]), bits<uint32_t>(s[r]), false, false);
+      s[r] = bits<float>(x[0]) + bits<float>(x[1]);
+    }
+    // Key 4bb + r of the chunk against query qj; past N or after the query
     // (causal) it is invisible.
     float mx = kNegInf;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int64_t key = k0 + 4 * b + r;
+      const int64_t key = k0 + 4 * bb + r;
       if (key >= N || (CAUSAL && key > qj)) s[r] = kNegInf;
       mx = fmaxf(mx, s[r]);
     }
@@ -402,55 +439,61 @@ __global__ void __launch_bounds__(kQ4Waves * 64, 1) fwd_f32_q4_kernel(KernelPara
     }
     lpart = lpart * alpha + rs;
 #pragma unroll
-    for (int cc = 0; cc < 16; ++cc) acc[cc] *= alpha;
+    for (int cc = 0; cc < 8; ++cc) acc[cc] *= alpha;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int cc = 0; cc < 16; ++cc)
-        acc[cc] = __builtin_amdgcn_mfma_f32_4x4x1f32(vf[16 * r + cc], pw[r], acc[cc], 0, 0, 0);
+      for (int cc = 0; cc < 8; ++cc)
+        acc[cc] = __builtin_amdgcn_mfma_f32_4x4x1f32(vf[8 * r + cc], pw[r], acc[cc], 0, 0, 0);
   };
 
-  // Chunks wave, wave + 4, ...: once a chunk's operands are in registers the
-  // next chunk's loads go out, then the products run.
-  for (int ch = wave; ch < n_chunks; ch += kQ4Waves) {
-    float kf[D], vf[64];
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's pieces have landed
-    read_chunk(kf, vf);
-    if (ch + kQ4Waves < n_chunks) issue_chunk(ch + kQ4Waves);
-    compute(kf, vf, ch);
+  for (int i = 0; i < n_mine; ++i) {
+    float kf[32], vf[32];
+    // Chunk i has landed when at most chunk i + 1's loads are outstanding.
+    if (i + 1 < n_mine)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * PIECES));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    read_chunk(i, kf, vf);
+    if (i + 2 < n_mine) {
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the buffer's reads are done
+      issue(i + 2);
+    }
+    compute(kf, vf, i);
   }
-  __syncthreads();  // every wave is done with its LDS area
+  __syncthreads();  // every wave is done with its LDS buffers
 
-  // Merge: each wave sums its partial O over the 16 blocks in registers; the
-  // lanes of block 0 then hold the wave's O for their query, which goes to LDS
-  // with the wave's maximum and sum.
-  const auto add = [](float x, float y) { return x + y; };
-  const float lq = query_reduce(lpart, add);
+  // Merge: each lane's partial O (its query j, its half and block) and
+  // partial sum go to LDS; thread t then forms output (q, d) = (t / 64,
+  // t % 64) over the 8 blocks and the 4 waves.  Both halves hold the same
+  // weights, so the sums come from half 0.
 #pragma unroll
-  for (int cc = 0; cc < 16; ++cc)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[cc][i] = query_reduce(acc[cc][i], add);
-  if (lane < kQ4Rows) {
-#pragma unroll
-    for (int cc = 0; cc < 16; ++cc)
-      *(float4*)&part[wave][lane][cc][0] = make_float4(acc[cc][0], acc[cc][1], acc[cc][2], acc[cc][3]);
-    m_lds[wave][lane] = m;
-    l_lds[wave][lane] = lq;
-  }
+  for (int cc = 0; cc < 8; ++cc) *(f32x4*)&part[wave][lane][4 * cc] = acc[cc];
+  l_lds[wave][lane] = lpart;
+  if (lane < kQ4Rows) m_lds[wave][lane] = m;
   __syncthreads();
-  if (tid < kQ4Rows * D) {
-    const int q = tid >> 6, d = tid & 63;  // one output element per thread
+  {
+    const int q = tid >> 6, d = tid & 63;
     const int64_t qi = q0 + q;
     float M = kNegInf;
 #pragma unroll
     for (int w = 0; w < kQ4Waves; ++w) M = fmaxf(M, m_lds[w][q]);
     const float M_use = M == kNegInf ? 0.f : M;
+    // Column d = 16 i + 8 h + c of O is register i of accumulator c in the
+    // lanes of half h.
+    const int hd = (d >> 3) & 1, e = (d & 7) * 4 + (d >> 4);
     float L = 0.f, o = 0.f;
 #pragma unroll
     for (int w = 0; w < kQ4Waves; ++w) {
       const float wt = __builtin_amdgcn_exp2f(m_lds[w][q] - M_use);
-      L += wt * l_lds[w][q];
-      o += wt * part[w][q][d & 15][d >> 4];
+      float lw = 0.f, aw = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 8; ++kb) {
+        lw += l_lds[w][4 * kb + q];
+        aw += part[w][32 * hd + 4 * kb + q][e];
+      }
+      L += wt * lw;
+      o += wt * aw;
     }
     if (qi < N) {
       ((float*)p.o)[(bh * N + qi) * D + d] = o / L;
