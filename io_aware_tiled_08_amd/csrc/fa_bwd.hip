@@ -500,18 +500,18 @@ __global__ void __launch_bounds__(kBwdWavesQ * 64, 1) bwd_dq_kernel(BwdParams p)
   using H = Half<T>;
   using Frag = typename H::Frag;
   using Pair = typename H::Pair;
-  using Ops = TileOps<T, D>;
   constexpr int RB = 2 * D;
   constexpr int TILE = kBwdTile * RB;
-  constexpr int NKS = D / 16;
-  constexpr int ND = D / 32;
+  constexpr int NKS = D / 32;   // 32-deep steps of a score product
+  constexpr int NDB = D / 16;   // 16-column blocks of dQ^T
   constexpr int NBQ = 3;  // K/V tiles in LDS: tile t + 2 loads while tile t is used
   __shared__ __attribute__((aligned(1024))) char smem[NBQ][2][TILE];  // [buffer][K, V]
 
   const int64_t N = p.N;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, hh = lane >> 5;
+  const int l16 = lane & 15;  // query of the lane within a 16-query block
+  const int lg = lane >> 4;   // 16-lane group: keys 4*lg .. of a 16-key block, or 8*lg .. of a 32-key step
   // XCD-aware order; causal: the longest query blocks (highest index) first.
   const int logical = xcd_order();
   const int64_t bh = logical / p.n_blk_q;
@@ -519,28 +519,30 @@ __global__ void __launch_bounds__(kBwdWavesQ * 64, 1) bwd_dq_kernel(BwdParams p)
   if (CAUSAL) qblk = p.n_blk_q - 1 - qblk;
   const int64_t q0 = (int64_t)qblk * BRQ;
   const int64_t qw = q0 + 32 * wave;
-  const int64_t qrow = qw + l32;
 
   const T* Qh = (const T*)p.q + bh * N * D;
   const T* Kh = (const T*)p.k + bh * N * D;
   const T* Vh = (const T*)p.v + bh * N * D;
   const T* dOh = (const T*)p.dout + bh * N * D;
 
-  // Q and dO of this lane's query (B operands of S^T = K Q^T, dP^T = V dO^T).
-  Frag qf[NKS], df[NKS];
-  float lse2 = 0.f, drow = 0.f;
-  {
-    const bool ok = qrow < N;
-    const T* qs_ = Qh + (ok ? qrow : 0) * D + 8 * hh;
-    const T* ds_ = dOh + (ok ? qrow : 0) * D + 8 * hh;
+  // Q and dO of the lane's two queries qw + 16*qb + l16 (B operands of
+  // S^T = K Q^T and dP^T = V dO^T): d = 32*ks + 8*lg .. +7.
+  Frag qf[2][NKS], df[2][NKS];
+  float lse2[2] = {0.f, 0.f}, drow[2] = {0.f, 0.f};
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int64_t qr = qw + 16 * qb + l16;
+    const bool ok = qr < N;
+    const T* qs_ = Qh + (ok ? qr : 0) * D + 8 * lg;
+    const T* ds_ = dOh + (ok ? qr : 0) * D + 8 * lg;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      qf[ks] = bits<Frag>(ok ? *(const u32x4*)(qs_ + 16 * ks) : u32x4{0, 0, 0, 0});
-      df[ks] = bits<Frag>(ok ? *(const u32x4*)(ds_ + 16 * ks) : u32x4{0, 0, 0, 0});
+      qf[qb][ks] = bits<Frag>(ok ? *(const u32x4*)(qs_ + 32 * ks) : u32x4{0, 0, 0, 0});
+      df[qb][ks] = bits<Frag>(ok ? *(const u32x4*)(ds_ + 32 * ks) : u32x4{0, 0, 0, 0});
     }
     if (ok) {
-      lse2 = p.lse[bh * N + qrow] * kLog2e;
-      drow = p.delta[bh * N + qrow];
+      lse2[qb] = p.lse[bh * N + qr] * kLog2e;
+      drow[qb] = p.delta[bh * N + qr];
     }
   }
 
@@ -560,11 +562,30 @@ __global__ void __launch_bounds__(kBwdWavesQ * 64, 1) bwd_dq_kernel(BwdParams p)
     stage_tile<D, NWQ>(Vh + r0 * D, 0, rows, lds_base + (buf * 2 + 1) * TILE, wave, lane);
   };
 
-  f32x16 dq[ND];
+  f32x4 dq[NDB][2];
 #pragma unroll
-  for (int db = 0; db < ND; ++db) dq[db] = f32x16{};
+  for (int db = 0; db < NDB; ++db) dq[db][0] = dq[db][1] = f32x4{};
   const float c = p.c;
-  const int krow = k_row_of_lane(l32);
+  // Row operand of 16-key block b (b = 0, 1 within a 32-key step): the lane
+  // feeds row m = l16 of the block with tile row 8*(m/4) + 4*b + m%4 (plus the
+  // step's 32), so that register r of lane group lg in the product holds key
+  // 8*lg + 4*b + r of the step: the 8 keys lane group lg contributes to the
+  // dQ product are 8 consecutive keys, 4 from each block.
+  const int krow = 8 * (l16 >> 2) + (l16 & 3);
+  auto row_frag = [&](const char* tile, int r, int ch) -> Frag {
+    return bits<Frag>(*(const u32x4*)(tile + r * RB + bswz<D>(r, ch) * 16));
+  };
+  // K^T operand of dQ^T block db for keys 8*lg .. +7 of the step at row0:
+  // lane j16 of group lg addresses row row0 + 8*lg + j16/4 (+4 for the second
+  // half) at columns 16*db + 4*(j16%4).
+  auto kt_frag = [&](const char* tile, int row0, int db) -> Frag {
+    const int col = 16 * db + 4 * (l16 & 3);
+    const int ch = col >> 3, off = (col & 7) * 2;
+    const int ra = row0 + 8 * lg + (l16 >> 2), rb = ra + 4;
+    const u32x2 lo = lds_read_tr(tile, ra * RB + bswz<D>(ra, ch) * 16 + off);
+    const u32x2 hi = lds_read_tr(tile, rb * RB + bswz<D>(rb, ch) * 16 + off);
+    return bits<Frag>(u32x4{lo[0], lo[1], hi[0], hi[1]});
+  };
 
   // Tiles 0 and 1 before the loop, tile t + 2 after the barrier of tile t
   // (into the buffer of tile t - 1, whose reads all precede that barrier).
@@ -574,12 +595,15 @@ __global__ void __launch_bounds__(kBwdWavesQ * 64, 1) bwd_dq_kernel(BwdParams p)
   issue(1);
   wait_loads<2 * LPW>();
 #pragma unroll
-  for (int ks = 0; ks < NKS; ++ks) {
-    fence(qf[ks]);
-    fence(df[ks]);
+  for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      fence(qf[qb][ks]);
+      fence(df[qb][ks]);
+    }
+    fence(lse2[qb]);
+    fence(drow[qb]);
   }
-  fence(lse2);
-  fence(drow);
   for (int t = 0; t < n_tiles; ++t) {
     wait_loads<2 * LPW>();  // tile t has landed; tile t + 1 may be in flight
     block_barrier();
@@ -590,63 +614,88 @@ __global__ void __launch_bounds__(kBwdWavesQ * 64, 1) bwd_dq_kernel(BwdParams p)
       const char* vtile = &smem[buf][1][0];
       const int64_t k0 = (int64_t)t * kBwdTile;
 #pragma unroll
-      for (int kb = 0; kb < kBwdTile / 32; ++kb) {
-        // S^T = K Q^T and dP^T = V dO^T: register r holds key
-        // k0 + 32*kb + key_of_reg(r, hh) of this lane's query.
-        f32x16 s = f32x16{}, dp = f32x16{};
+      for (int st = 0; st < kBwdTile / 32; ++st) {
+        // S^T = K Q^T and dP^T = V dO^T for the step's two 16-key blocks:
+        // register r of block b holds key 8*lg + 4*b + r of the step.
+        f32x4 s[2][2], dp[2][2];
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          s = H::mma(Ops::row(ktile, 32 * kb + krow, 2 * ks + hh), qf[ks], s);
-          dp = H::mma(Ops::row(vtile, 32 * kb + krow, 2 * ks + hh), df[ks], dp);
-        }
-        float pr[16];
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -lse2));
-        // Key kbase + kr (kr = key_of_reg(r, hh)) is visible iff kr < N - kbase,
-        // the query exists, and, when causal, kr <= qrow - kbase.  The bound
-        // is shifted by 8*hh so that kr becomes the constant key_of_reg(r, 0).
-        const int64_t kbase = k0 + 32 * kb;
+          for (int qb = 0; qb < 2; ++qb) s[b][qb] = dp[b][qb] = f32x4{};
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks) {
+            const int r = 32 * st + 4 * b + krow;
+            const Frag ak = row_frag(ktile, r, 4 * ks + lg);
+            const Frag av = row_frag(vtile, r, 4 * ks + lg);
+#pragma unroll
+            for (int qb = 0; qb < 2; ++qb) {
+              s[b][qb] = mma16<T>(ak, qf[qb][ks], s[b][qb]);
+              dp[b][qb] = mma16<T>(av, df[qb][ks], dp[b][qb]);
+            }
+          }
+        // Key kbase + kr (kr = 8*lg + 4*b + r) is visible iff kr < N - kbase,
+        // the query exists, and, when causal, kr <= query - kbase.
+        const int64_t kbase = k0 + 32 * st;
         const bool full = kbase + 32 <= N && qw + 32 <= N && (!CAUSAL || kbase + 31 <= qw);
-        if (__builtin_expect(!full, 0)) {
-          int64_t hi64 = qrow < N ? N - kbase : 0;
-          if (CAUSAL && qrow - kbase + 1 < hi64) hi64 = qrow - kbase + 1;
-          const int hi = (int)(hi64 < 0 ? 0 : (hi64 > 32 ? 32 : hi64)) - 8 * hh;
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (key_of_reg(r, 0) >= hi) pr[r] = 0.f;
-        }
         Frag sf[2];
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
+        for (int qb = 0; qb < 2; ++qb) {
+          float pr[2][4];
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              pr[b][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[b][qb][r], c, -lse2[qb]));
+          if (__builtin_expect(!full, 0)) {
+            const int64_t qr = qw + 16 * qb + l16;
+            int64_t hi64 = qr < N ? N - kbase : 0;
+            if (CAUSAL && qr - kbase + 1 < hi64) hi64 = qr - kbase + 1;
+            const int hi = (int)(hi64 < 0 ? 0 : (hi64 > 32 ? 32 : hi64)) - 8 * lg;
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (4 * b + r >= hi) pr[b][r] = 0.f;
+          }
+          // dS^T as the B operand of dQ^T += K^T dS^T: keys 8*lg + 0..7.
           u32x4 fs;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 8 * jj + 2 * e;
-            fs[e] = bits<uint32_t>(H::pack(pr[r] * (dp[r] - drow), pr[r + 1] * (dp[r + 1] - drow)));
-          }
-          sf[jj] = bits<Frag>(fs);
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const int r = 2 * e;
+              fs[2 * b + e] = bits<uint32_t>(H::pack(pr[b][r] * (dp[b][qb][r] - drow[qb]),
+                                                     pr[b][r + 1] * (dp[b][qb][r + 1] - drow[qb])));
+            }
+          sf[qb] = bits<Frag>(fs);
         }
         // dQ^T += K^T dS^T.
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
+        for (int db = 0; db < NDB; ++db) {
+          const Frag a = kt_frag(ktile, 32 * st, db);
 #pragma unroll
-          for (int db = 0; db < ND; ++db)
-            dq[db] = H::mma(Ops::rows_t(ktile, 32 * kb + 16 * jj, db, lane), sf[jj], dq[db]);
+          for (int qb = 0; qb < 2; ++qb) dq[db][qb] = mma16<T>(a, sf[qb], dq[db][qb]);
+        }
       }
     }
   }
   wait_loads<0>();  // the empty loads past the end land before the workgroup ends
 
-  if (qrow < N) {
-    T* dst = (T*)p.dq + (bh * N + qrow) * D + 4 * hh;
+  // Lane (l16, lg) holds dQ[query][16*db + 4*lg .. +3] of query qw + 16*qb + l16.
 #pragma unroll
-    for (int db = 0; db < ND; ++db)
+  for (int qb = 0; qb < 2; ++qb) {
+    const int64_t qr = qw + 16 * qb + l16;
+    if (qr < N) {
+      T* dst = (T*)p.dq + (bh * N + qr) * D + 4 * lg;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const Pair a = H::pack(dq[db][4 * g] * p.scale, dq[db][4 * g + 1] * p.scale);
-        const Pair b = H::pack(dq[db][4 * g + 2] * p.scale, dq[db][4 * g + 3] * p.scale);
-        *(u32x2*)(dst + db * 32 + 8 * g) = u32x2{bits<uint32_t>(a), bits<uint32_t>(b)};
+      for (int db = 0; db < NDB; ++db) {
+        const Pair a = H::pack(dq[db][qb][0] * p.scale, dq[db][qb][1] * p.scale);
+        const Pair b2 = H::pack(dq[db][qb][2] * p.scale, dq[db][qb][3] * p.scale);
+        *(u32x2*)(dst + 16 * db) = u32x2{bits<uint32_t>(a), bits<uint32_t>(b2)};
       }
+    }
   }
 }
 
