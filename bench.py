@@ -171,31 +171,49 @@ def _baseline_record(value, unit, workers, sample):
             "host_cores": cores, "cpu_model": model}
 
 
-def cpu_baseline(w, q, k, v, budget_s: float):
+def cpu_baseline(w, q, k, v, budget_s: float, gpu_out=None):
     """Times the fp64 oracle on the workload's own inputs in blocks of 512
     query rows (heads in order, rows in order) on a thread pool over the host's
     cores, starting blocks until the budget is spent.  FLOPs are counted per
-    row from the number of keys the row sees (4*d per visible key)."""
+    row from the number of keys the row sees (4*d per visible key).  With
+    gpu_out = (O, LSE), the GPU's outputs on the host, the record also gives
+    the largest absolute difference of O and of LSE from the oracle over the
+    rows the oracle computed."""
+    import threading
+
     import numpy as np
 
     import oracle
     block = 512
     units = [(b, h, r0) for b in range(w.B) for h in range(w.H) for r0 in range(0, w.N, block)]
+    err = {"O": 0.0, "LSE": 0.0}
+    lock = threading.Lock()
 
     def run(u):
         b, h, r0 = u
         sl = (slice(b, b + 1), slice(h, h + 1))
         idx = np.arange(r0, min(r0 + block, w.N), dtype=np.int64)
-        oracle.attention_forward(q[sl], k[sl], v[sl], w.scale, w.causal, rows=idx)
+        O_ref, L_ref = oracle.attention_forward(q[sl], k[sl], v[sl], w.scale, w.causal, rows=idx)
+        if gpu_out is not None:
+            eo = float(np.max(np.abs(gpu_out[0][b, h, idx].astype(np.float64) - O_ref[0, 0])))
+            el_ = float(np.max(np.abs(gpu_out[1][b, h, idx].astype(np.float64) - L_ref[0, 0])))
+            with lock:
+                err["O"] = max(err["O"], eo)
+                err["LSE"] = max(err["LSE"], el_)
         visible = (idx + 1) if w.causal else np.full(idx.shape, w.N)
         return 4.0 * w.d * float(visible.sum())
 
     flops, n, el, workers = run_oracle_pool(units, run, budget_s)
     rows_done = sum(min(block, w.N - units[i][2]) for i in range(n))
-    return _baseline_record(
+    rec = _baseline_record(
         flops / el / 1e12, "TFLOP/s", workers,
         f"{rows_done} of {w.B * w.H * w.N} query rows of {w.name} (the first {n} blocks of "
         f"{block} rows, heads in order), fp64 numpy, {workers} threads, {el:.1f} s")
+    rec["seconds"] = round(el, 2)
+    rec["rows"] = rows_done
+    if gpu_out is not None:
+        rec["max_abs_err"] = {"O": err["O"], "LSE": err["LSE"], "rows": rows_done}
+    return rec
 
 
 def _counter_rows(path, counter):
@@ -612,6 +630,75 @@ def calibrate(seconds: float = 1.5) -> None:
         measure(f"mfma_chain_f16_{label}", chain, 20, float(blocks) * 8 * iters * 131072)
 
 
+# The configurations of the forward path side by side (bench.py --all-configs):
+# (label, workload, extra bench.py arguments).  The single-head fp32 kernel is
+# shorter than a launch from Python, so its steps run as one captured graph.
+ALL_CONFIGS = (
+    ("C1", "single_head_f32", ("--graph",)),
+    ("C2 non-causal", "batch_f16_d64", ()),
+    ("C2 causal", "batch_f16_d64_causal", ()),
+    ("C3 (headline)", "headline_f16_d128", ()),
+    ("C4", "rescale_stress_bf16", ()),
+    ("C5", "long_context_bf16", ()),
+)
+
+
+def all_configs(steps: int, budget_s: float, out_path: str) -> str:
+    """Runs bench.py once per configuration of ALL_CONFIGS, each in a child
+    process, and writes one table of them to out_path: GPU rate and share of
+    the MFMA peak, HBM GB/s of compulsory and of counter-measured bytes (the
+    committed traffic profile, when the kernel source matches), the largest
+    difference of O and LSE from the fp64 oracle over the rows the CPU
+    baseline computed, and that baseline's time and threads."""
+    import subprocess
+    recs = []
+    for label, wl, extra in ALL_CONFIGS:
+        cmd = [sys.executable, os.path.abspath(__file__), "--workload", wl, "--steps", str(steps),
+               "--cpu-budget", str(budget_s), *extra]
+        print(f"step: {label} ({wl})", flush=True)
+        r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True,
+                           timeout=600)
+        if r.returncode != 0:
+            raise SystemExit(f"{wl} failed ({r.returncode}):\n{r.stderr[-2000:]}")
+        line = [x for x in r.stdout.splitlines() if x.startswith("{")][-1]
+        print(line, flush=True)
+        recs.append((label, json.loads(line)))
+    text = format_all_configs(recs, steps, budget_s)
+    with open(out_path, "w") as f:
+        f.write(text)
+    return text
+
+
+def format_all_configs(recs, steps: int, budget_s: float) -> str:
+    """The markdown table of all_configs from (label, bench JSON record) pairs."""
+    cmdline = (f"python3 bench.py --all-configs --steps {steps} --cpu-budget {budget_s:g}")
+    out = ["# All forward configurations side by side", "",
+           "Command (GPU host, repository root; one bench.py child process per configuration):", "",
+           f"    {cmdline}", "",
+           "GB/s columns are bytes per launch over the event-timed kernel time: compulsory bytes "
+           "(every input read once, every output written once) and counter-measured HBM bytes "
+           "(`profiles/traffic_<workload>.md`, FETCH_SIZE + WRITE_SIZE calibrated against a "
+           "copy of known size), as fractions of 8 TB/s.  Errors are max |GPU - oracle| over the "
+           "rows the CPU baseline computed (fp64 oracle on the same inputs).", "",
+           "| config | workload | GPU TFLOP/s | % of MFMA peak | compulsory GB/s (of 8 TB/s) | "
+           "counter GB/s (of 8 TB/s) | max abs err O / LSE (rows) | oracle CPU s (threads) |",
+           "|---|---|---|---|---|---|---|---|"]
+    for label, r in recs:
+        rf = r["roofline"]
+        ms = rf["kernel_ms"]
+        comp = rf["compulsory_bytes"] / (ms * 1e-3) / 1e9
+        cnt = rf.get("traffic")
+        cnt_s = (f"{cnt / (ms * 1e-3) / 1e9:.0f} ({cnt / (ms * 1e-3) / 8e12:.1%})"
+                 if cnt else "n/a")
+        cb = r.get("cpu_baseline") or {}
+        err = cb.get("max_abs_err")
+        err_s = (f"{err['O']:.2e} / {err['LSE']:.2e} ({err['rows']})" if err else "n/a")
+        cpu_s = (f"{cb.get('seconds', float('nan')):.1f} ({cb.get('cores')})" if cb else "n/a")
+        out.append(f"| {label} | `{r['config']['workload']}` | {r['value']:.1f} | {rf['frac']:.1%} | "
+                   f"{comp:.0f} ({comp / 8000:.1%}) | {cnt_s} | {err_s} | {cpu_s} |")
+    return "\n".join(out) + "\n"
+
+
 def cpu_baseline_cache(w, q, k, v, budget_s: float):
     """Times the fp64 oracle on a key/value-cache workload, whole (b, h) heads
     on a thread pool over the host's cores until the budget is spent; the rate
@@ -678,6 +765,9 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="time the steps as one captured HIP graph (square forward workloads): "
                          "removes host launch gaps for kernels shorter than a launch")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="run every forward configuration (C1-C5) in child processes and write "
+                         "profiles/all_configs.md")
     ap.add_argument("--calibrate", action="store_true",
                     help="print the card's sustained fp16 GEMM and register-only MFMA throughput "
                          "with clock and power, then exit")
@@ -703,6 +793,11 @@ def main():
         return
     if args.calibrate:
         calibrate()
+        return
+    if args.all_configs:
+        print(all_configs(args.steps, args.cpu_budget,
+                          os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                                       "all_configs.md")))
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the forward pass "
@@ -975,7 +1070,10 @@ def main():
             qx, kx, vx = (oracle.dequantize_fp8(x, s) for x, s in ((q, qs), (k, ks), (v, vs)))
             result["cpu_baseline"] = cpu_baseline(w, qx, kx, vx, args.cpu_budget)
         else:
-            result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget)
+            # The last timed call's outputs, compared with the oracle on the
+            # rows the baseline computes.
+            gpu_out = (o.float().cpu().numpy(), lse.cpu().numpy())
+            result["cpu_baseline"] = cpu_baseline(w, q, k, v, args.cpu_budget, gpu_out)
     else:
         result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)

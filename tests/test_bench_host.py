@@ -102,6 +102,47 @@ def test_cpu_baseline_counts_the_threads_it_used():
     assert rec["sample"].startswith(f"{w.N} of {w.N} query rows")
 
 
+def test_cpu_baseline_reports_the_difference_from_given_outputs():
+    """With the GPU's outputs handed in, the record gives max |O - oracle| and
+    max |LSE - oracle| over the rows it computed: zero for the oracle's own
+    outputs, and exactly a planted offset otherwise."""
+    import numpy as np
+
+    import oracle
+    w = W.WORKLOADS["single_head_f32"]
+    q, k, v = W.workload_inputs(w)
+    O, L = oracle.attention_forward(q, k, v, w.scale, w.causal)
+    rec = bench.cpu_baseline(w, q, k, v, 5.0, gpu_out=(O.copy(), L.copy()))
+    assert rec["max_abs_err"] == {"O": 0.0, "LSE": 0.0, "rows": w.N}
+    O2, L2 = O.copy(), L.copy()
+    O2[0, 0, 300, 5] += 0.25
+    L2[0, 0, 7] -= 0.125
+    rec = bench.cpu_baseline(w, q, k, v, 5.0, gpu_out=(O2, L2))
+    assert rec["max_abs_err"]["O"] == pytest.approx(0.25, abs=1e-12)
+    assert rec["max_abs_err"]["LSE"] == pytest.approx(0.125, abs=1e-12)
+    assert rec["rows"] == w.N and rec["seconds"] > 0
+    assert "max_abs_err" not in bench.cpu_baseline(w, q, k, v, 0.1)
+    assert np.isfinite(rec["value"])
+
+
+def test_all_configs_table():
+    """One row per configuration, with compulsory and counter GB/s over the
+    kernel time, the oracle differences and the baseline's seconds."""
+    rec = {"value": 1200.0, "config": {"workload": "headline_f16_d128"},
+           "roofline": {"kernel_ms": 0.25, "compulsory_bytes": 1e8, "traffic": 2e8, "frac": 0.477},
+           "cpu_baseline": {"seconds": 1.25, "cores": 16,
+                            "max_abs_err": {"O": 1e-4, "LSE": 2e-5, "rows": 4096}}}
+    text = bench.format_all_configs([("C3 (headline)", rec)], 100, 30.0)
+    row = [x for x in text.splitlines() if x.startswith("| C3")][0]
+    assert "| 1200.0 | 47.7% |" in row
+    assert "400 (5.0%)" in row and "800 (10.0%)" in row  # 1e8 and 2e8 bytes in 0.25 ms
+    assert "1.00e-04 / 2.00e-05 (4096)" in row and "1.2 (16)" in row
+    assert "--all-configs --steps 100 --cpu-budget 30" in text
+    assert [c[1] for c in bench.ALL_CONFIGS] == [
+        "single_head_f32", "batch_f16_d64", "batch_f16_d64_causal", "headline_f16_d128",
+        "rescale_stress_bf16", "long_context_bf16"]
+
+
 def test_oracle_pool_stops_starting_units_after_the_budget():
     import time as _t
     seen = []
