@@ -18,8 +18,9 @@
 //   * bwd_dkdv: a workgroup owns 128 keys in four groups of 32 and runs eight
 //     waves; the two waves of a key group share a SIMD.  One ("P wave", K in
 //     registers) computes S = Q K^T, P and dV^T += dO^T P; the other ("dS
-//     wave", V in registers) computes dP = dO V^T, takes P from LDS and
-//     accumulates dK^T += Q^T dS.  With K (or V) as the B operand a lane owns
+//     wave", V in registers) computes dP = dO V^T, takes P from LDS (rounded
+//     to the input type: the values of the dV product) and accumulates
+//     dK^T += Q^T dS.  With K (or V) as the B operand a lane owns
 //     one key and the 16 queries of a 32x32 block sit in its registers, so P
 //     and dS feed the next products as B operands straight from registers.
 //     32-query tiles of Q and dO (with their LSE and D) are staged through
@@ -167,12 +168,24 @@ __device__ __forceinline__ void block_barrier() {
 // For each 32-query tile the P wave computes S = Q K^T (K in registers),
 // P = exp2(c S - LSE log2 e) and dV^T += dO^T P; the dS wave computes
 // dP = dO V^T (V in registers), takes P from its partner through LDS, and
-// accumulates dK^T += Q^T dS with dS = P (dP - D).  One workgroup barrier per
+// accumulates dK^T += Q^T dS with dS = P (dP - D).  P crosses in the input
+// type (the packed values of the dV product, half the bytes of fp32): dS is
+// then formed from the rounded P, which adds u |dS| to its error bound.  One workgroup barrier per
 // tile separates "P written" from "P read"; while one wave of a SIMD runs its
 // vector work the other issues matrix products.  Q/dO tiles and their LSE and
 // D rows are loaded into LDS kDkvBufs - 1 tiles ahead.
 constexpr int kDkvQ = 32;    // queries per staged tile
 constexpr int kDkvBufs = 6;  // staged tiles: tile t + 5 loads while tile t is used
+
+// The two values of a packed 16-bit pair, widened exactly to fp32 (a bf16
+// value is the upper half of an fp32 pattern).
+template <typename T>
+__device__ __forceinline__ f32x2 unpack_pair(uint32_t w) {
+  if constexpr (std::is_same_v<T, __bf16>)
+    return f32x2{bits<float>(w << 16), bits<float>(w & 0xffff0000u)};
+  else
+    return __builtin_convertvector(bits<f16x2>(w), f32x2);
+}
 
 // vmcnt(n) and lgkmcnt(0): at most n of this wave's vector-memory loads still
 // outstanding, and every LDS access of this wave complete.
@@ -201,9 +214,10 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
   constexpr int ND = D / 32;
   __shared__ __attribute__((aligned(1024))) char smem[NB][2][TILE];  // [buffer][Q, dO]
   __shared__ __attribute__((aligned(16))) float stat[NB][2][QT];     // [buffer][LSE log2 e, D]
-  // P of the current tile, per key group and slot (tile parity): 4 chunks of
-  // 64 lanes x 4 floats, so each 16-byte access of a wave covers 1 KiB.
-  __shared__ __attribute__((aligned(1024))) float xch[4][2][4][64 * 4];
+  // P of the current tile, per key group and slot (tile parity), packed in
+  // the input type: 2 chunks of 64 lanes x 4 words (8 values), so each
+  // 16-byte access of a wave covers 1 KiB.
+  __shared__ __attribute__((aligned(1024))) uint32_t xch[4][2][2][64 * 4];
 
   const int64_t N = p.N;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -302,7 +316,7 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
     const u32x2 hi = lds_read_tr(tile, toff[i][1]);
     return bits<Frag>(u32x4{lo[0], lo[1], hi[0], hi[1]});
   };
-  float* xlane = &xch[kg][0][0][0] + lane * 4;  // this lane's P slots: + slot*1024 + chunk*256
+  uint32_t* xlane = &xch[kg][0][0][0] + lane * 4;  // this lane's P slots: + slot*512 + chunk*256
 
   // Tiles qt_begin .. qt_begin + NB - 2 before the loop (tile qt_begin + i
   // in buffer i % NB); tile t + NB - 1 after the barrier of tile t.  The
@@ -327,7 +341,7 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
     constexpr int buf = decltype(bufc)::value;
     const char* qtile = &smem[buf][0][0];
     const char* dotile = &smem[buf][1][0];
-    float* xs = xlane + (buf & 1) * 1024;
+    uint32_t* xs = xlane + (buf & 1) * 512;
     const int64_t qbase = (int64_t)qt * QT;
     // live: some query of the tile sees a key of the group (always, when
     // not causal; written as a run-time test there too, which keeps the
@@ -381,15 +395,13 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
           }
         }
 #pragma unroll
-        for (int ch = 0; ch < 4; ++ch)
-          *(float4*)(xs + ch * 256) = float4{pr[4 * ch], pr[4 * ch + 1], pr[4 * ch + 2], pr[4 * ch + 3]};
-#pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
           u32x4 f;
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             f[e] = bits<uint32_t>(H::pack(pr[8 * jj + 2 * e], pr[8 * jj + 2 * e + 1]));
           pf[jj] = bits<Frag>(f);
+          *(u32x4*)(xs + jj * 256) = f;
         }
       } else {
         dp = sd;
@@ -416,12 +428,14 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
         const float* dt = &stat[buf][1][0];
         float pr[16], dl[16];
 #pragma unroll
-        for (int ch = 0; ch < 4; ++ch) {
-          const float4 x = *(const float4*)(xs + ch * 256);
-          pr[4 * ch] = x.x;
-          pr[4 * ch + 1] = x.y;
-          pr[4 * ch + 2] = x.z;
-          pr[4 * ch + 3] = x.w;
+        for (int jj = 0; jj < 2; ++jj) {
+          const u32x4 x = *(const u32x4*)(xs + jj * 256);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const f32x2 w = unpack_pair<T>(x[e]);
+            pr[8 * jj + 2 * e] = w[0];
+            pr[8 * jj + 2 * e + 1] = w[1];
+          }
         }
 #pragma unroll
         for (int half = 0; half < 2; ++half) {

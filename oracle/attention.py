@@ -433,24 +433,30 @@ def attention_backward(q, k, v, do, scale: float, causal: bool = False):
 
 
 def backward_error_bound(q, k, v, do, scale: float, causal: bool = False, u: float = 2.0 ** -11,
-                         u_o: Optional[float] = None):
+                         u_o: Optional[float] = None, u_p: Optional[float] = None):
     """Per-element bounds on |dQ_hat - dQ|, |dK_hat - dK|, |dV_hat - dV| for a
     backward pass that (1) rounds P to a type with unit roundoff u before
-    dV = P^T dO, (2) forms dS = P (dP - D) in fp32 with D = rowsum(dO * O_in)
-    where O_in is the forward output rounded to unit u_o (default u), and (3)
-    rounds dS to unit u before dQ = scale dS K and dK = scale dS^T Q.  Inputs
-    are exact (already in the 16-bit type); products of 16-bit values and
-    fp32 sums are exact up to fp32 accumulation, which is left to the caller's
-    absolute slack.
+    dV = P^T dO, (2) forms dS = P_in (dP - D) in fp32 with D = rowsum(dO * O_in),
+    where O_in is the forward output rounded to unit u_o (default u) and P_in
+    is P rounded to unit u_p (default u: the rounded P of step 1; 0 for P in
+    fp32), and (3) rounds dS to unit u before dQ = scale dS K and
+    dK = scale dS^T Q.  Inputs are exact (already in the 16-bit type);
+    products of 16-bit values and fp32 sums are exact up to fp32
+    accumulation, which is left to the caller's absolute slack.
 
     Derivation.  |P_hat - P| <= u P gives |dV_hat - dV|_jc <= u sum_i P_ij |dO_ic|.
-    O_in = O (1 + e), |e| <= u_o, so |D_hat - D|_i <= u_o sum_c |dO_ic O_ic| =: dD_i,
-    and dS_hat = round(P (dP - D_hat)) differs from dS by at most
-    P_ij dD_i + u (|dS_ij| + P_ij dD_i) =: e_ij.  Then
-    |dQ_hat - dQ|_ic <= scale sum_j e_ij |K_jc| and
-    |dK_hat - dK|_jc <= scale sum_i e_ij |Q_ic|.
+    O_in = O (1 + e), |e| <= u_o, so |D_hat - D|_i <= u_o sum_c |dO_ic O_ic| =: dD_i.
+    With P_in = P (1 + a), |a| <= u_p, and the rounding of dS (1 + b), |b| <= u,
+    dS_hat = P (1 + a)(dP - D - (D_hat - D))(1 + b), so with g = (1 + u_p)(1 + u)
+    it differs from dS = P (dP - D) by at most
+    (g - 1) |dS_ij| + g P_ij dD_i =: e_ij  (u_p = 0: P_ij dD_i + u (|dS_ij| + P_ij dD_i)).
+    Then |dQ_hat - dQ|_ic <= scale sum_j e_ij |K_jc| and
+    |dK_hat - dK|_jc <= scale sum_i e_ij |Q_ic|.  A pass that forms dS from a
+    less rounded P (smaller u_p) stays within the bound.
     """
     u_o = u if u_o is None else u_o
+    u_p = u if u_p is None else u_p
+    g = (1.0 + u_p) * (1.0 + u)
     Q, K, V, dO = as_f64(q), as_f64(k), as_f64(v), as_f64(do)
     B, H, N, d = Q.shape
     s64 = abs(boundary_scale(scale))
@@ -466,7 +472,7 @@ def backward_error_bound(q, k, v, do, scale: float, causal: bool = False, u: flo
             Dv = (dO[b, h] * O).sum(axis=1)
             dS = P * (dO[b, h] @ V[b, h].T - Dv[:, None])
             dD = u_o * np.abs(dO[b, h] * O).sum(axis=1)
-            e = P * dD[:, None] + u * (np.abs(dS) + P * dD[:, None])
+            e = (g - 1.0) * np.abs(dS) + g * P * dD[:, None]
             bV[b, h] = u * (P.T @ np.abs(dO[b, h]))
             bQ[b, h] = s64 * (e @ np.abs(K[b, h]))
             bK[b, h] = s64 * (e.T @ np.abs(Q[b, h]))
@@ -474,7 +480,8 @@ def backward_error_bound(q, k, v, do, scale: float, causal: bool = False, u: flo
 
 
 def attention_backward_sampled(q, k, v, do, scale: float, causal: bool, heads, rows, cols,
-                               u: float = 2.0 ** -11, u_o: Optional[float] = None):
+                               u: float = 2.0 ** -11, u_o: Optional[float] = None,
+                               u_p: Optional[float] = None):
     """attention_backward and backward_error_bound restricted to chosen
     entries, for inputs too large to differentiate whole: for each (b, h) in
     `heads`, dQ and its bound at query rows `rows`, and dK, dV and their
@@ -487,6 +494,8 @@ def attention_backward_sampled(q, k, v, do, scale: float, causal: bool, heads, r
     dV[cols], bQ[rows], bK[cols], bV[cols])}.
     """
     u_o = u if u_o is None else u_o
+    u_p = u if u_p is None else u_p
+    g = (1.0 + u_p) * (1.0 + u)
     Q, K, V, dO = as_f64(q), as_f64(k), as_f64(v), as_f64(do)
     B, H, N, d = Q.shape
     s = boundary_scale(scale)
@@ -505,8 +514,8 @@ def attention_backward_sampled(q, k, v, do, scale: float, causal: bool, heads, r
         # rows of dS (for dQ) and columns of dS (for dK); P's columns give dV
         dS_r = P[rows] * (dO[b, h][rows] @ V[b, h].T - Dv[rows, None])
         dS_c = P[:, cols] * (dO[b, h] @ V[b, h][cols].T - Dv[:, None])
-        e_r = P[rows] * dD[rows, None] + u * (np.abs(dS_r) + P[rows] * dD[rows, None])
-        e_c = P[:, cols] * dD[:, None] + u * (np.abs(dS_c) + P[:, cols] * dD[:, None])
+        e_r = (g - 1.0) * np.abs(dS_r) + g * P[rows] * dD[rows, None]
+        e_c = (g - 1.0) * np.abs(dS_c) + g * P[:, cols] * dD[:, None]
         out[(b, h)] = (s * (dS_r @ K[b, h]), s * (dS_c.T @ Q[b, h]), P[:, cols].T @ dO[b, h],
                        abs(s) * (e_r @ np.abs(K[b, h])), abs(s) * (e_c.T @ np.abs(Q[b, h])),
                        u * (P[:, cols].T @ np.abs(dO[b, h])))

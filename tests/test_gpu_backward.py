@@ -4,8 +4,8 @@ The kernel receives the forward output O rounded to the input type and the
 exact LSE in float32, as flash_attn_fwd would hand them over.  Accuracy
 contract (oracle.backward_error_bound): the bound per element that follows
 from rounding P, dS and O to the input type (unit u = 2^-11 for fp16, 2^-8
-for bf16), plus the rounding of dq, dk, dv themselves (u |ref|) and fp32
-accumulation (1e-5 max|ref| + 1e-6).
+for bf16), dS being formed from the rounded P, plus the rounding of dq, dk,
+dv themselves (u |ref|) and fp32 accumulation (1e-5 max|ref| + 1e-6).
 """
 import math
 

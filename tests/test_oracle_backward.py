@@ -121,16 +121,10 @@ def _round16(x, dtype):
     return torch.from_numpy(np.ascontiguousarray(x)).to(dtype).to(torch.float64).numpy()
 
 
-@pytest.mark.parametrize("dtype,u", [(torch.float16, 2.0 ** -11), (torch.bfloat16, 2.0 ** -8)])
-@pytest.mark.parametrize("causal", [False, True])
-def test_backward_bound_holds_for_simulated_rounding(dtype, u, causal):
-    """Simulate the 16-bit pass: O handed in rounded, P and dS rounded before
-    the products; the error never exceeds the bound and reaches a fair part
-    of it."""
-    q, k, v, do = (_round16(_randn(1400 + t, 1, 2, 64, 32), dtype) for t in range(4))
-    scale = 1.0 / math.sqrt(32)
-    dQ, dK, dV, _ = oracle.attention_backward(q, k, v, do, scale, causal)
-    bQ, bK, bV = oracle.backward_error_bound(q, k, v, do, scale, causal, u=u)
+def _simulated_pass(q, k, v, do, scale, causal, dtype, p_rounded):
+    """The 16-bit pass in float64: O handed in rounded, P rounded before
+    dV = P^T dO, dS = P_in (dP - D) rounded before dQ and dK, with P_in the
+    rounded P (p_rounded) or P itself."""
     s = oracle.boundary_scale(scale)
     N = q.shape[2]
     S = np.einsum("bhid,bhjd->bhij", q, k) * s
@@ -141,15 +135,53 @@ def test_backward_bound_holds_for_simulated_rounding(dtype, u, causal):
     O = _round16(P @ v, dtype)
     D = (do * O).sum(-1)
     Ph = _round16(P, dtype)
-    dSh = _round16(P * (do @ np.swapaxes(v, -1, -2) - D[..., None]), dtype)
-    sims = {"dV": np.swapaxes(Ph, -1, -2) @ do, "dQ": s * dSh @ k,
+    dSh = _round16((Ph if p_rounded else P) * (do @ np.swapaxes(v, -1, -2) - D[..., None]), dtype)
+    return {"dV": np.swapaxes(Ph, -1, -2) @ do, "dQ": s * dSh @ k,
             "dK": s * np.swapaxes(dSh, -1, -2) @ q}
+
+
+@pytest.mark.parametrize("p_rounded", [False, True])
+@pytest.mark.parametrize("dtype,u", [(torch.float16, 2.0 ** -11), (torch.bfloat16, 2.0 ** -8)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_bound_holds_for_simulated_rounding(dtype, u, causal, p_rounded):
+    """Simulate the 16-bit pass, with P entering dS in fp32 (u_p = 0) or
+    rounded to the input type (u_p = u, the default): the error never exceeds
+    the bound and reaches a fair part of it."""
+    q, k, v, do = (_round16(_randn(1400 + t, 1, 2, 64, 32), dtype) for t in range(4))
+    scale = 1.0 / math.sqrt(32)
+    dQ, dK, dV, _ = oracle.attention_backward(q, k, v, do, scale, causal)
+    bQ, bK, bV = oracle.backward_error_bound(q, k, v, do, scale, causal, u=u,
+                                             u_p=u if p_rounded else 0.0)
+    sims = _simulated_pass(q, k, v, do, scale, causal, dtype, p_rounded)
     worst = 0.0
     for name, ref, b in (("dQ", dQ, bQ), ("dK", dK, bK), ("dV", dV, bV)):
         err = np.abs(sims[name] - ref)
         assert np.all(err <= b * (1 + 1e-9) + 1e-13), name
         worst = max(worst, float(np.max(err / (b + 1e-300))))
     assert worst > 0.05
+
+
+@pytest.mark.parametrize("dtype,u", [(torch.float16, 2.0 ** -11), (torch.bfloat16, 2.0 ** -8)])
+def test_backward_bound_needs_the_rounded_p_term(dtype, u):
+    """With K the identity (N = d), dQ is scale * dS, so the dQ bound is the
+    per-element bound on dS itself.  A pass that forms dS from the rounded P
+    then leaves the bound without the P-rounding term (u_p = 0) and stays
+    inside it with the term; a pass that forms dS from P in fp32 stays inside
+    both.  Scores stay within a few units, so no weight is subnormal in the
+    16-bit type (the bound treats every rounding as relative)."""
+    n = 32
+    rng = np.random.default_rng(11)
+    q, v, do = (_round16(rng.standard_normal((1, 2, n, n)), dtype) for _ in range(3))
+    k = np.broadcast_to(np.eye(n), (1, 2, n, n)).copy()
+    scale = 0.5
+    dQ = oracle.attention_backward(q, k, v, do, scale, False)[0]
+    b_fp32_p = oracle.backward_error_bound(q, k, v, do, scale, False, u=u, u_p=0.0)[0]
+    b_rounded_p = oracle.backward_error_bound(q, k, v, do, scale, False, u=u)[0]
+    rounded = np.abs(_simulated_pass(q, k, v, do, scale, False, dtype, True)["dQ"] - dQ)
+    fp32 = np.abs(_simulated_pass(q, k, v, do, scale, False, dtype, False)["dQ"] - dQ)
+    assert np.any(rounded > b_fp32_p * (1 + 1e-6))
+    assert np.all(rounded <= b_rounded_p * (1 + 1e-9) + 1e-13)
+    assert np.all(fp32 <= b_fp32_p * (1 + 1e-9) + 1e-13)
 
 
 @pytest.mark.parametrize("causal", [False, True])
