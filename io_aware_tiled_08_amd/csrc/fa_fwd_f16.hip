@@ -70,6 +70,22 @@
 namespace fa {
 namespace {
 
+// Row maxima of both 16-query blocks of a wave at once: a and b are a lane's
+// partial maxima (its column of block 0 and of block 1); on return each holds
+// the maximum over the four lane groups l, l^16, l^32, l^48.  One lane swap
+// between the halves leaves block 0's pair maxima in lanes 0-31 and block
+// 1's in lanes 32-63, one 16-lane swap finishes both, and a last swap hands
+// each lane both results: three swaps and two maxima instead of four and four.
+__device__ __forceinline__ void quad_max_pair(float& a, float& b) {
+  const auto h = __builtin_amdgcn_permlane32_swap(bits<uint32_t>(a), bits<uint32_t>(b), false, false);
+  const float m = fmaxf(bits<float>(h[0]), bits<float>(h[1]));
+  const auto q = __builtin_amdgcn_permlane16_swap(bits<uint32_t>(m), bits<uint32_t>(m), false, false);
+  const float m2 = fmaxf(bits<float>(q[0]), bits<float>(q[1]));
+  const auto r = __builtin_amdgcn_permlane32_swap(bits<uint32_t>(m2), bits<uint32_t>(m2), false, false);
+  a = bits<float>(r[0]);
+  b = bits<float>(r[1]);
+}
+
 // The whole pass from the Q load to the O and LSE stores, for one 256-row
 // query block (work item wi) of one (batch, head), or, with STREAM, for the
 // R unmasked items j0, j0 + stride, ... (head-major) run back to back as one
@@ -470,10 +486,11 @@ __device__ __forceinline__ void fwd_f16_tiles(const KernelParams& p, const WorkI
     float mxc[2];
     bool grow[2];
 #pragma unroll
+    for (int qb = 0; qb < 2; ++qb) mxc[qb] = chain_max4<NKB * 4>([&](int i) { return s[i / 4][qb][i % 4]; });
+    quad_max_pair(mxc[0], mxc[1]);
+#pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      float mx = chain_max4<NKB * 4>([&](int i) { return s[i / 4][qb][i % 4]; });
-      mx = quad_max(mx);
-      mxc[qb] = mx * c;  // c > 0, so -inf stays -inf
+      mxc[qb] *= c;  // c > 0, so -inf stays -inf
       grow[qb] = mxc[qb] > m[qb] + kRescaleSlack;
     }
     if (__ballot(grow[0] || grow[1])) {
