@@ -19,7 +19,10 @@
 // longest-first order packs the CUs evenly.  The price is twice the K/V tile
 // traffic per row (each tile serves 128 rows), and four LDS buffers per
 // tensor (the groups read different tiles at once): 128 KiB at d = 64, which is
-// why the schedule is used for d = 64 only.
+// why the schedule is used for d = 64 only.  Each workgroup runs two blocks of
+// one head back to back, block n_qblk - 1 - i and then block i: their lengths
+// add up to the same tile count for every pair, so one workgroup per pair
+// balances by construction and a CU does not wait for a second dispatch.
 #include "fa_device.h"
 #include "fa_f16_common.h"
 #include "fa_launch.h"
@@ -27,8 +30,9 @@
 namespace fa {
 namespace {
 
+// One 128-row block (work item wi), from its Q load to its O and LSE stores.
 template <typename T, int D, bool CAUSAL>
-__global__ void __launch_bounds__(512, 1) fwd_f16_ks_kernel(KernelParams p) {
+__device__ __forceinline__ void ks_block(const KernelParams& p, const WorkItem wi) {
   using H = Half<T>;
   using Frag = typename H::Frag;
   using Pair = typename H::Pair;
@@ -49,7 +53,6 @@ __global__ void __launch_bounds__(512, 1) fwd_f16_ks_kernel(KernelParams p) {
 
   __shared__ __attribute__((aligned(1024))) char smem[2][4][TILE];  // [K, V][buffer]
 
-  const WorkItem wi = work_item<CAUSAL>(p.n_qblk);
   const int64_t N = p.N;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -398,6 +401,29 @@ __global__ void __launch_bounds__(512, 1) fwd_f16_ks_kernel(KernelParams p) {
   }
 }
 
+// Two blocks of one head per workgroup, run back to back: block i and block
+// n_qblk - 1 - i (equal total length under the causal mask).
+template <typename T, int D, bool CAUSAL>
+__global__ void __launch_bounds__(512, 1) fwd_f16_ks_pair_kernel(KernelParams p) {
+  const int pairs = (p.n_qblk + 1) / 2;  // per head
+  const int nblk = gridDim.x, wg = blockIdx.x;
+  const int logical = (nblk % 8 == 0) ? (wg % 8) * (nblk / 8) + wg / 8 : wg;
+  WorkItem w;
+  w.bh = logical / pairs;
+  const int i = logical % pairs;
+  w.qblk = p.n_qblk - 1 - i;  // the longer block first
+  ks_block<T, D, CAUSAL>(p, w);
+  if (i != p.n_qblk - 1 - i) {
+    // The first block's merge reads LDS that the second block's first tile
+    // loads overwrite.
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    w.qblk = i;
+    ks_block<T, D, CAUSAL>(p, w);
+  }
+}
+
 template <typename T, int D, bool CAUSAL>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   constexpr int BR = 128;
@@ -415,8 +441,8 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   // exp2(0) = 1.
   p.c = __builtin_fmaxf(__builtin_fabsf(a.scale) * kLog2e, 1.17549435e-38f);
   p.q_sign = a.scale < 0.f ? 0x80008000u : 0u;
-  hipLaunchKernelGGL((fwd_f16_ks_kernel<T, D, CAUSAL>), dim3((unsigned)(a.BH * p.n_qblk)), dim3(512),
-                     0, stream, p);
+  hipLaunchKernelGGL((fwd_f16_ks_pair_kernel<T, D, CAUSAL>),
+                     dim3((unsigned)(a.BH * ((p.n_qblk + 1) / 2))), dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 
