@@ -170,10 +170,11 @@ __device__ __forceinline__ void block_barrier() {
 // dP = dO V^T (V in registers), takes P from its partner through LDS, and
 // accumulates dK^T += Q^T dS with dS = P (dP - D).  P crosses in the input
 // type (the packed values of the dV product, half the bytes of fp32): dS is
-// then formed from the rounded P, which adds u |dS| to its error bound.  One workgroup barrier per
-// tile separates "P written" from "P read"; while one wave of a SIMD runs its
-// vector work the other issues matrix products.  Q/dO tiles and their LSE and
-// D rows are loaded into LDS kDkvBufs - 1 tiles ahead.
+// then formed from the rounded P, which adds u |dS| to its error bound.  One
+// workgroup barrier per tile separates "P written" from "P read"; while one
+// wave of a SIMD runs its vector work the other issues matrix products.
+// Q/dO tiles and their LSE and D rows are loaded into LDS kDkvBufs - 1 tiles
+// ahead.
 constexpr int kDkvQ = 32;    // queries per staged tile
 constexpr int kDkvBufs = 6;  // staged tiles: tile t + 5 loads while tile t is used
 
