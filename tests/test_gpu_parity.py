@@ -227,6 +227,20 @@ def test_workload_long_context():
     assert torch.isfinite(o).all() and torch.isfinite(lse).all()
 
 
+@pytest.mark.parametrize("N", [600, 700])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_causal_d64_block_pairs(dtype, N):
+    """The small causal d=64 schedule runs 128-row blocks in pairs (block
+    n-1-i, then block i, in one workgroup): an odd block count (600: five
+    blocks, the middle one alone), a ragged last block (700: six blocks, 60
+    rows in the last), and a grid of 45 workgroups (not a multiple of the
+    eight XCDs), every row against the oracle."""
+    q, k, v = W.random_qkv(3, 5, N, 64, dtype, seed=2200 + N)
+    scale = W.default_scale(64)
+    o, lse = gpu_forward(q, k, v, scale, True)
+    check(o, lse, q, k, v, scale, True, dtype, label=f"{dtype} causal d=64 N={N} block pairs")
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_causal_d64_many_blocks(dtype):
     """Causal d=64 with more than 512 blocks of 256 rows (here 640): the
