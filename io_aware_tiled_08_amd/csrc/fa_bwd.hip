@@ -24,10 +24,13 @@
 //     one key and the 16 queries of a 32x32 block sit in its registers, so P
 //     and dS feed the next products as B operands straight from registers.
 //     32-query tiles of Q and dO (with their LSE and D) are staged through
-//     LDS five tiles ahead.
+//     LDS five tiles ahead.  Causal: a workgroup runs key blocks i and
+//     n - 1 - i one after the other, so that the triangle's work is spread
+//     evenly over the workgroups.
 //   * bwd_dq: a workgroup owns 256 queries (8 waves x 32); it walks 64-key
 //     tiles of K and V and accumulates dQ^T += K^T dS^T with S^T = K Q^T
-//     (lane = query, as in the forward kernel).
+//     (lane = query, as in the forward kernel).  Causal: query blocks
+//     n - 1 - i and i share a workgroup, as the key blocks above do.
 // Every tile is read both by rows (MFMA A operands) and transposed
 // (ds_read_b64_tr_b16, for the d x rows operands); one XOR permutation of the
 // 16-byte chunks of a row serves both without LDS bank conflicts.
@@ -200,7 +203,7 @@ __device__ __forceinline__ void wait_loads_lds() {
 }
 
 template <typename T, int D, bool CAUSAL>
-__global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
+__device__ __forceinline__ void dkdv_block(const BwdParams& p, const int64_t bh, const int kblk) {
   using H = Half<T>;
   using Frag = typename H::Frag;
   using Pair = typename H::Pair;
@@ -226,10 +229,6 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
   const bool prole = wave < 4;
   const int kg = wave & 3;
   const int l32 = lane & 31, hh = lane >> 5;
-  // XCD-aware order (the blocks of one head share an XCD's L2).
-  const int logical = xcd_order();
-  const int64_t bh = logical / p.n_blk;
-  const int kblk = logical % p.n_blk;
   const int64_t k0 = (int64_t)kblk * kBwdRows;
   const int64_t kw = k0 + 32 * kg;  // the key group's first key
   const int64_t key = kw + l32;     // this lane's key (B-operand column)
@@ -507,9 +506,29 @@ __global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
   }
 }
 
+// XCD-aware order (the blocks of one head share an XCD's L2). Causal: two key
+// blocks of one head per workgroup, back to back, block i and then block
+// n - 1 - i, so that every workgroup has about the same number of query tiles.
+template <typename T, int D, bool CAUSAL>
+__global__ void __launch_bounds__(512, 1) bwd_dkdv_kernel(BwdParams p) {
+  const int logical = xcd_order();
+  if constexpr (!CAUSAL) {
+    dkdv_block<T, D, CAUSAL>(p, logical / p.n_blk, logical % p.n_blk);
+  } else {
+    const int pairs = (p.n_blk + 1) / 2;
+    const int64_t bh = logical / pairs;
+    const int i = logical % pairs;
+    dkdv_block<T, D, CAUSAL>(p, bh, i);
+    if (i != p.n_blk - 1 - i) {
+      block_barrier();  // every wave's reads of the first block's tiles are done
+      dkdv_block<T, D, CAUSAL>(p, bh, p.n_blk - 1 - i);
+    }
+  }
+}
+
 // ---- dQ ----------------------------------------------------------------------
 template <typename T, int D, bool CAUSAL>
-__global__ void __launch_bounds__(kBwdWavesQ * 64, 1) bwd_dq_kernel(BwdParams p) {
+__device__ __forceinline__ void dq_block(const BwdParams& p, const int64_t bh, const int qblk) {
   constexpr int NWQ = kBwdWavesQ;
   constexpr int BRQ = 32 * NWQ;  // queries per workgroup
   using H = Half<T>;
@@ -527,11 +546,6 @@ __global__ void __launch_bounds__(kBwdWavesQ * 64, 1) bwd_dq_kernel(BwdParams p)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15;  // query of the lane within a 16-query block
   const int lg = lane >> 4;   // 16-lane group: keys 4*lg .. of a 16-key block, or 8*lg .. of a 32-key step
-  // XCD-aware order; causal: the longest query blocks (highest index) first.
-  const int logical = xcd_order();
-  const int64_t bh = logical / p.n_blk_q;
-  int qblk = logical % p.n_blk_q;
-  if (CAUSAL) qblk = p.n_blk_q - 1 - qblk;
   const int64_t q0 = (int64_t)qblk * BRQ;
   const int64_t qw = q0 + 32 * wave;
 
@@ -714,6 +728,26 @@ __global__ void __launch_bounds__(kBwdWavesQ * 64, 1) bwd_dq_kernel(BwdParams p)
   }
 }
 
+// XCD-aware order. Causal: two query blocks of one head per workgroup, back to
+// back, block n - 1 - i and then block i, so that every workgroup has about
+// the same number of visible key tiles.
+template <typename T, int D, bool CAUSAL>
+__global__ void __launch_bounds__(kBwdWavesQ * 64, 1) bwd_dq_kernel(BwdParams p) {
+  const int logical = xcd_order();
+  if constexpr (!CAUSAL) {
+    dq_block<T, D, CAUSAL>(p, logical / p.n_blk_q, logical % p.n_blk_q);
+  } else {
+    const int pairs = (p.n_blk_q + 1) / 2;
+    const int64_t bh = logical / pairs;
+    const int i = logical % pairs;
+    dq_block<T, D, CAUSAL>(p, bh, p.n_blk_q - 1 - i);
+    if (i != p.n_blk_q - 1 - i) {
+      block_barrier();  // every wave's reads of the first block's tiles are done
+      dq_block<T, D, CAUSAL>(p, bh, i);
+    }
+  }
+}
+
 template <typename T, int D, bool CAUSAL>
 hipError_t launch(const BwdArgs& a, hipStream_t stream) {
   BwdParams p;
@@ -739,11 +773,11 @@ hipError_t launch(const BwdArgs& a, hipStream_t stream) {
                      stream, p, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const unsigned grid = (unsigned)(a.BH * p.n_blk);
+  const unsigned grid = (unsigned)(a.BH * (CAUSAL ? (p.n_blk + 1) / 2 : p.n_blk));
   hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, CAUSAL>), dim3(grid), dim3(512), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3((unsigned)(a.BH * p.n_blk_q)),
+  hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL>), dim3((unsigned)(a.BH * (CAUSAL ? (p.n_blk_q + 1) / 2 : p.n_blk_q))),
                      dim3(kBwdWavesQ * 64), 0, stream, p);
   return hipGetLastError();
 }

@@ -77,6 +77,20 @@ def test_backward_many_tiles(causal):
     check(got, q, k, v, do, W.default_scale(128), causal, "bf16", f"N=1000 causal={causal}")
 
 
+@pytest.mark.parametrize("N", [600, 700])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_backward_causal_block_pairs(dtype, d, N):
+    """Causal: a workgroup takes blocks i and n - 1 - i.  N = 600 gives 5 key
+    blocks and 3 query blocks (an odd middle block runs alone), N = 700 gives
+    6 and 3, both with a ragged last block; B*H = 15, so the grid is not a
+    multiple of the eight XCDs either.  Every gradient against the oracle."""
+    q, k, v = W.random_qkv(3, 5, N, d, dtype, seed=7300 + N + d)
+    do = W.random_dout(3, 5, N, d, dtype, seed=7300 + N + d)
+    got = run_bwd(q, k, v, do, W.default_scale(d), True, dtype)
+    check(got, q, k, v, do, W.default_scale(d), True, dtype, f"pairs {dtype} d={d} N={N}")
+
+
 def test_backward_deterministic_and_side_stream():
     q, k, v = W.random_qkv(1, 2, 333, 128, "f16", seed=7300)
     do = W.random_dout(1, 2, 333, 128, "f16", seed=7300)
