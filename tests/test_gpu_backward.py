@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import oracle
-from io_aware_tiled_08_amd import FlashAttnError, flash_attn_bwd
+from io_aware_tiled_08_amd import FlashAttnError, flash_attn_bwd, lib
 from io_aware_tiled_08_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -98,6 +98,46 @@ def test_backward_deterministic_and_side_stream():
     b = run_bwd(q, k, v, do, 0.088, True, "f16", stream=torch.cuda.Stream())
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_graph_capture_replays(causal):
+    """flash_attn_bwd with a caller workspace enqueues three kernels, allocates
+    nothing and clears no memory, so it can be captured in a HIP graph: three
+    replays, with eager backward calls on other tensors between them, each
+    bitwise equal to the eager call."""
+    B, H, N, d = 1, 3, 700, 128
+    q, k, v = W.random_qkv(B, H, N, d, "f16", seed=7400)
+    do = W.random_dout(B, H, N, d, "f16", seed=7400)
+    scale = W.default_scale(d)
+    O, L = oracle.attention_forward(q, k, v, scale, causal)
+    o = torch.from_numpy(O).to(torch.float16).to(DEV)
+    lse = torch.from_numpy(L).to(torch.float32).to(DEV)
+    qd, kd, vd, dod = (x.to(DEV) for x in (q, k, v, do))
+    ws = torch.empty(lib().flash_attn_bwd_workspace_size(B, H, N), dtype=torch.uint8, device=DEV)
+    ref = run_bwd(q, k, v, do, scale, causal, "f16")
+    grads = [torch.empty_like(qd) for _ in range(3)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up call on the capture stream
+        flash_attn_bwd(qd, kd, vd, o, lse, dod, *grads, scale=scale, causal=causal, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        flash_attn_bwd(qd, kd, vd, o, lse, dod, *grads, scale=scale, causal=causal, workspace=ws)
+    for rep in range(3):
+        for g in grads:
+            g.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, g, r in zip(("dQ", "dK", "dV"), grads, ref):
+            assert torch.equal(g, r), f"replay {rep} {name}"
+        # unrelated eager work between replays (one head, its own workspace)
+        other = run_bwd(q[:, :1], k[:, :1], v[:, :1], do[:, :1], scale, causal, "f16")
+        for g, r in zip(other, ref):
+            assert torch.equal(g, r[:, :1])
 
 
 def test_backward_workspace_and_dtype_errors():

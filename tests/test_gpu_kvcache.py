@@ -146,3 +146,39 @@ def test_cache_workload_full(name):
     q, k, v = W.cache_workload_inputs(w)
     o, lse = run_cache(q, k, v, w.scale, w.causal)
     check(o, lse, q, k, v, w.scale, w.causal, w.dtype, name)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_cache_graph_capture_replays(causal):
+    """With a caller workspace the cache path enqueues the split and merge
+    kernels, allocates nothing and clears no memory, so it can be captured in
+    a HIP graph: three replays, with eager cache calls on other tensors
+    between them, each bitwise equal to the eager call."""
+    B, H, Nq, Nk, d = 2, 4, 3, 5000, 128
+    q, k, v = W.random_cache_inputs(B, H, Nq, Nk, d, "bf16", seed=8800)
+    scale = W.default_scale(d)
+    assert kvcache_splits(B, H, Nq, Nk, d, 0) > 1
+    ws = torch.empty(kvcache_workspace_size(B, H, Nq, Nk, d, 0), dtype=torch.uint8, device=DEV)
+    o_ref, lse_ref = run_cache(q, k, v, scale, causal)
+    qd, kd, vd = (x.to(DEV) for x in (q, k, v))
+    o = torch.empty_like(qd)
+    lse = torch.empty(B, H, Nq, dtype=torch.float32, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up call on the capture stream
+        flash_attn_fwd_kvcache(qd, kd, vd, o, lse, scale=scale, causal=causal, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        flash_attn_fwd_kvcache(qd, kd, vd, o, lse, scale=scale, causal=causal, workspace=ws)
+    for rep in range(3):
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(lse, lse_ref), f"replay {rep}"
+        # unrelated eager work between replays (other queries, its own workspace)
+        o2, _ = run_cache(q.flip(2), k, v, scale, causal)
+        assert torch.isfinite(o2).all()
