@@ -538,7 +538,7 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const int64_t bh, c
   constexpr int TILE = kBwdTile * RB;
   constexpr int NKS = D / 32;   // 32-deep steps of a score product
   constexpr int NDB = D / 16;   // 16-column blocks of dQ^T
-  constexpr int NBQ = 3;  // K/V tiles in LDS: tile t + 2 loads while tile t is used
+  constexpr int NBQ = 4;  // K/V tiles in LDS: tile t + 3 loads while tile t is used
   __shared__ __attribute__((aligned(1024))) char smem[NBQ][2][TILE];  // [buffer][K, V]
 
   const int64_t N = p.N;
@@ -616,13 +616,14 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const int64_t bh, c
     return bits<Frag>(u32x4{lo[0], lo[1], hi[0], hi[1]});
   };
 
-  // Tiles 0 and 1 before the loop, tile t + 2 after the barrier of tile t
+  // Tiles 0 to 2 before the loop, tile t + 3 after the barrier of tile t
   // (into the buffer of tile t - 1, whose reads all precede that barrier).
   // The register loads above land with tile 0.
   constexpr int LPW = TILE / 1024 / NWQ;
   issue(0);
   issue(1);
-  wait_loads<2 * LPW>();
+  issue(2);
+  wait_loads<4 * LPW>();
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
@@ -634,9 +635,9 @@ __device__ __forceinline__ void dq_block(const BwdParams& p, const int64_t bh, c
     fence(drow[qb]);
   }
   for (int t = 0; t < n_tiles; ++t) {
-    wait_loads<2 * LPW>();  // tile t has landed; tile t + 1 may be in flight
+    wait_loads<4 * LPW>();  // tile t has landed; tiles t + 1, t + 2 may be in flight
     block_barrier();
-    issue(t + 2);
+    issue(t + 3);
     if (t < wave_tiles) {
       const int buf = t % NBQ;
       const char* ktile = &smem[buf][0][0];
