@@ -24,7 +24,7 @@
 //     one key and the 16 queries of a 32x32 block sit in its registers, so P
 //     and dS feed the next products as B operands straight from registers.
 //     32-query tiles of Q and dO (with their LSE and D) are staged through
-//     LDS five tiles ahead.  Causal: a workgroup runs key blocks i and
+//     LDS three tiles ahead.  Causal: a workgroup runs key blocks i and
 //     n - 1 - i one after the other, so that the triangle's work is spread
 //     evenly over the workgroups.
 //   * bwd_dq: a workgroup owns 256 queries (8 waves x 32); it walks 64-key
@@ -179,7 +179,7 @@ __device__ __forceinline__ void block_barrier() {
 // Q/dO tiles and their LSE and D rows are loaded into LDS kDkvBufs - 1 tiles
 // ahead.
 constexpr int kDkvQ = 32;    // queries per staged tile
-constexpr int kDkvBufs = 6;  // staged tiles: tile t + 5 loads while tile t is used
+constexpr int kDkvBufs = 4;  // staged tiles: tile t + 3 loads while tile t is used
 
 // The two values of a packed 16-bit pair, widened exactly to fp32 (a bf16
 // value is the upper half of an fp32 pattern).
@@ -476,13 +476,9 @@ __device__ __forceinline__ void dkdv_block(const BwdParams& p, const int64_t bh,
       step(role, std::integral_constant<int, 2>{}, qt0 + 2);
       if (qt0 + 3 >= qt_end) break;
       step(role, std::integral_constant<int, 3>{}, qt0 + 3);
-      if (qt0 + 4 >= qt_end) break;
-      step(role, std::integral_constant<int, 4>{}, qt0 + 4);
-      if (qt0 + 5 >= qt_end) break;
-      step(role, std::integral_constant<int, 5>{}, qt0 + 5);
     }
   };
-  static_assert(NB == 6, "the tile loop above is written out for six buffers");
+  static_assert(NB == 4, "the tile loop above is written out for four buffers");
   if (prole)
     tiles(std::true_type{});
   else
